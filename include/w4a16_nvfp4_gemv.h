@@ -1,0 +1,159 @@
+/*
+ * w4a16_nvfp4_gemv -- small-M BF16 x NVFP4 (W4A16) GEMV for AMD MI355X (gfx950).
+ *
+ * C ABI of libw4a16_nvfp4_gemv.so.  Every entry point takes plain device
+ * pointers and sizes, enqueues its kernels asynchronously on `stream` (a
+ * hipStream_t; NULL means the legacy default stream) and returns a status
+ * code.  The library never allocates device memory, never synchronizes the
+ * stream and never aborts: a call that cannot run returns a non-zero status
+ * and enqueues nothing.  All buffers are owned by the caller and must stay
+ * alive until the enqueued work has finished.
+ *
+ * Data formats (the "ModelOpt layout" of the pages vllm.models.flint.ops.
+ * nvfp4_gemv, module docstring, and vllm.models.flint.ops.linear,
+ * _swizzled_scale_buffer):
+ *   bf16 tensors    uint16_t bit patterns of IEEE bfloat16.
+ *   packed weight   uint8_t [N][K/2], two FP4 E2M1 codes per byte, the LOW
+ *                   nibble holding the even k.
+ *   block scales    one FP8 E4M3FN byte per 16 consecutive k of a row, in
+ *                   the FLAT 128x4-swizzled buffer of
+ *                   ceil(N/128)*128 * ceil(K/64)*4 bytes: 512-byte tiles of
+ *                   128 rows x 4 scale columns, ordered by 128-row band and
+ *                   then by column group; inside a tile, row r lives in the
+ *                   16-byte chunk r%32 at byte (r/32)*4 + column%4.
+ *   global scale    one FP32 value in DEVICE memory (read by the kernel).
+ *
+ * Numerics (nvfp4_gemv page, module docstring "Numerics"): each weight is
+ * decoded exactly (e2m1 * e4m3 is always a BF16 value), products with the
+ * BF16 activations are accumulated in FP32, the FP32 global scale multiplies
+ * the FP32 accumulator and the result is rounded to BF16 once (round to
+ * nearest even).  The FP32 summation order is unspecified.
+ *
+ * Shape limits shared by the GEMV entry points: 0 <= M <= 32 tokens (M == 0
+ * is a successful no-op), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
+ * Pointer alignment: activations and weights 16 bytes, scales 4 bytes,
+ * outputs 4 bytes; the row stride ldx of x is a multiple of 8 elements.
+ */
+#ifndef W4A16_NVFP4_GEMV_H
+#define W4A16_NVFP4_GEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define W4A16_OK 0
+#define W4A16_ERR_INVALID_ARG 1   /* null pointer, negative or inconsistent size */
+#define W4A16_ERR_MISALIGNED 2    /* a pointer or stride breaks the alignment rules */
+#define W4A16_ERR_UNSUPPORTED 3   /* valid request outside the supported shapes */
+#define W4A16_ERR_HIP 4           /* the HIP runtime refused a launch */
+
+/* Largest token count of the GEMV entry points. */
+#define W4A16_MAX_M 32
+
+/*
+ * nvfp4_gemv -- out[M][N] = bf16(fp32(x @ dequant(W)^T) * global_scale).
+ * Defined on the nvfp4_gemv page (function nvfp4_gemv and the module
+ * docstring).
+ *   x            bf16 [M][ldx] (device), the first K columns are used.
+ *   w            uint8 [N][K/2] packed E2M1 codes (device).
+ *   w_scale      flat 128x4-swizzled E4M3 scales of the [N][K] weight (device).
+ *   global_scale one FP32 value (device).
+ *   silu_mul     0: out is bf16 [M][N].
+ *                1: the N rows are [gate | up] halves; out is bf16 [M][N/2]
+ *                   with out[m][j] = bf16(silu(g) * u), g and u the BF16
+ *                   GEMV outputs of rows j and N/2 + j, SiLU in FP32.
+ *                   Needs N % 32 == 0.
+ *   out          bf16 output, contiguous (device).
+ */
+int nvfp4_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+               const uint8_t *w, const uint8_t *w_scale, const float *global_scale,
+               int64_t N, int silu_mul, uint16_t *out, void *stream);
+
+/*
+ * bf16_gemv -- the same GEMV with a row-major BF16 weight w [N][K] (device)
+ * and a global scale of one (nvfp4_gemv page, function bf16_gemv).
+ * Arguments and limits as nvfp4_gemv, except K % 8 == 0 suffices.
+ */
+int bf16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+              const uint16_t *w, int64_t N, int silu_mul, uint16_t *out, void *stream);
+
+/*
+ * dequantize_rows -- out[rows][K] = bf16(e2m1 * e4m3), bit-exact, global
+ * scale not applied (nvfp4_gemv page, function dequantize_rows).
+ * Needs rows % 16 == 0 and K % 256 == 0 (the page's assertion).
+ *   w        uint8 [rows][K/2] (device), 16-byte aligned.
+ *   w_scale  flat 128x4-swizzled scales of the [rows][K] weight (device).
+ *   out      bf16 [rows][K] (device), 16-byte aligned.
+ */
+int dequantize_rows(const uint8_t *w, const uint8_t *w_scale, int64_t rows, int64_t K,
+                    uint16_t *out, void *stream);
+
+/*
+ * nvfp4_unswizzle_scales -- out[n][c] = the scale of row n, column c (= k/16)
+ * read from the flat 128x4-swizzled buffer; bit-exact.  Exposes the scale
+ * addressing the GEMV kernels use (the 128x4 layout named on the
+ * nvfp4_gemv page, nvfp4_gemv argument weight_scale).  Needs K % 16 == 0.
+ *   out  uint8 [N][K/16] (device).
+ */
+int nvfp4_unswizzle_scales(const uint8_t *w_scale, int64_t N, int64_t K, uint8_t *out,
+                           void *stream);
+
+/*
+ * moe_gate_up -- routed and shared expert gate/up projections of the MoE
+ * decode block in one launch (moe_gemv page, function gate_up).
+ *   x        bf16 [M][H] (device); ids int32 [M][topk] expert ids, each in
+ *            [0, E) (device; not validated: ids outside the range are a
+ *            caller error and are clamped into range by the kernel).
+ *   w1       uint8 [E][2I][H/2]: expert e's [gate; up] rows; w1_scale holds
+ *            E consecutive flat 128x4 buffers of the [2I][H] weight;
+ *            alpha FP32 [E] (device).
+ *   act      bf16 [M*topk][I] output: for pair p = t*topk + j and e = ids[p],
+ *            act[p][i] = bf16(silu(g) * u) with g, u the FP32 accumulators of
+ *            rows i and I+i of W1[e] times alpha[e] (not rounded to BF16).
+ *   wsh      uint8 [2SI][H/2] shared [gate; up] weight, ssh its flat scales,
+ *            gssh FP32 [1] (device).
+ *   sact     bf16 [M][SI] output: the nvfp4_gemv silu_mul result of the
+ *            shared expert.
+ * Limits: 0 <= M <= 32 (M == 0 is a no-op), 1 <= topk <= 16, E >= 1,
+ * H % 64 == 0, I % 16 == 0, SI % 16 == 0.
+ */
+int moe_gate_up(const uint16_t *x, int64_t M, int64_t H, const int32_t *ids, int64_t topk,
+                int64_t E, const uint8_t *w1, const uint8_t *w1_scale, const float *alpha,
+                int64_t I, uint16_t *act, const uint8_t *wsh, const uint8_t *ssh,
+                const float *gssh, int64_t SI, uint16_t *sact, void *stream);
+
+/*
+ * moe_down_combine -- top-k down projections, shared-expert down projection
+ * and the weighted combine in one launch (moe_gemv page, function
+ * down_combine):
+ *   y_j   = bf16(act[t*topk+j] . W2[e_j][h] * alpha2[e_j])
+ *   out   = bf16(bf16(sum_j tw[t][j] * y_j) + bf16(sact[t] . Wsd[h] * gssd))
+ * with the sum over j in FP32.
+ *   act bf16 [M*topk][I], ids int32 [M][topk], tw FP32 [M][topk] (device).
+ *   w2 uint8 [E][H][I/2] with E consecutive flat scale buffers of the
+ *   [H][I] weight in w2_scale; alpha2 FP32 [E].
+ *   sact bf16 [M][SI]; wsd uint8 [H][SI/2], ssd its flat scales, gssd FP32 [1].
+ *   out bf16 [M][H] (device).
+ * Limits: as moe_gate_up, with H % 16 == 0, I % 64 == 0, SI % 64 == 0.
+ */
+int moe_down_combine(const uint16_t *act, const int32_t *ids, const float *tw, int64_t M,
+                     int64_t topk, int64_t E, const uint8_t *w2, const uint8_t *w2_scale,
+                     const float *alpha2, int64_t H, int64_t I, const uint16_t *sact,
+                     const uint8_t *wsd, const uint8_t *ssd, const float *gssd, int64_t SI,
+                     uint16_t *out, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *w4a16_status_string(int status);
+
+/* Detail of the last failed call on this host thread (static per-thread
+ * storage; empty after a successful call). */
+const char *w4a16_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_NVFP4_GEMV_H */

@@ -173,3 +173,71 @@ def assert_close_bits(got_bits, want_bits, bound, what: str, nan_ok: bool = Fals
 
 def math_fsum_rows(x: np.ndarray) -> np.ndarray:
     return np.array([math.fsum(r) for r in x])
+
+
+# ---------------------------------------------------------------- checks used by the GPU parity tests
+def check_gemv(gpu_bits, acc, absacc, gs, k, what):
+    """GPU BF16 GEMV output against the oracle's binary64 accumulator: the
+    acceptance bound (one ulp + 1e-3 sum|xw| |gs|) and the tighter bound every
+    FP32 summation order meets.  Returns the worst |diff| / tight bound."""
+    ref = acc * float(gs)
+    got = bf16_bits_to_f64(gpu_bits)
+    diff = np.abs(got - ref)
+    bad = ~(diff <= gemv_bound(ref, absacc, gs))
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside the acceptance bound; "
+                             f"first at {i}: got {got[i]!r} oracle {ref[i]!r}")
+    tight = fp32_order_bound(ref, absacc, gs, k)
+    bad = ~(diff <= tight)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside the FP32-order bound; "
+                             f"first at {i}: got {got[i]!r} oracle {ref[i]!r}")
+    return float(np.max(diff / tight)) if diff.size else 0.0
+
+
+def check_silu(gpu_bits, oracle_bits, acc, absacc, gs, what, rounded_gate_up=True):
+    """GPU bf16(silu(g) * u) against the oracle, with the GEMV error of g and u
+    (rows j and H + j of acc) propagated through silu(g) * u."""
+    h = acc.shape[1] // 2
+    g_ref = acc[:, :h] * float(gs)
+    u_ref = acc[:, h:] * float(gs)
+    if rounded_gate_up:
+        bg = 1.5 * ulp_bf16(g_ref) + 1e-3 * float(gs) * absacc[:, :h]
+        bu = 1.5 * ulp_bf16(u_ref) + 1e-3 * float(gs) * absacc[:, h:]
+    else:
+        bg = 1e-3 * abs(float(gs)) * absacc[:, :h]
+        bu = 1e-3 * abs(float(gs)) * absacc[:, h:]
+    want = bf16_bits_to_f64(oracle_bits)
+    bound = silu_bound(want, g_ref, u_ref, bg, bu)
+    return assert_close_bits(gpu_bits, oracle_bits, bound, what)
+
+
+def check_routed_act(gpu_bits, oracle_bits, acc_r, abs_r, alpha_per_pair, what):
+    """Routed gate_up output: g, u are FP32 accumulators times alpha (not rounded)."""
+    h = acc_r.shape[1] // 2
+    a = np.asarray(alpha_per_pair, np.float64)[:, None]
+    g_ref = acc_r[:, :h] * a
+    u_ref = acc_r[:, h:] * a
+    bg = 1e-3 * a * abs_r[:, :h] + 2.0 ** -126
+    bu = 1e-3 * a * abs_r[:, h:] + 2.0 ** -126
+    want = bf16_bits_to_f64(oracle_bits)
+    return assert_close_bits(gpu_bits, oracle_bits, silu_bound(want, g_ref, u_ref, bg, bu), what)
+
+
+def check_down(gpu_bits, oracle_bits, acc_r, abs_r, acc_s, abs_s, tw, alpha2_per_slot, gssd, what):
+    """down_combine: out = bf16(bf16(sum_j tw_j y_j) + y_sh); the bound adds the
+    propagated GEMV bounds of every y_j and of y_sh, the rounding of the sum and
+    the FP32 error of the weighted sum."""
+    a2 = np.asarray(alpha2_per_slot, np.float64)[:, :, None]     # [M, topk, 1]
+    twv = np.asarray(tw, np.float64)[:, :, None]
+    y_ref = acc_r * a2
+    b_y = 1.5 * ulp_bf16(y_ref) + 1e-3 * a2 * abs_r
+    s_ref = np.sum(twv * y_ref, axis=1)
+    ysh_ref = acc_s * float(gssd)
+    b_sh = 1.5 * ulp_bf16(ysh_ref) + 1e-3 * float(gssd) * abs_s
+    want = bf16_bits_to_f64(oracle_bits)
+    bound = (2 * ulp_bf16(want) + 1.5 * ulp_bf16(s_ref) + np.sum(np.abs(twv) * b_y, axis=1)
+             + b_sh + 2.0 ** -22 * np.sum(np.abs(twv * y_ref), axis=1))
+    return assert_close_bits(gpu_bits, oracle_bits, bound, what)

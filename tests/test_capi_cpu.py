@@ -1,0 +1,131 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+function the header declares, and rejects bad arguments before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from w4a16_nvfp4_gemv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16_nvfp4_gemv.h")
+
+OK, INVALID, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["nvfp4_gemv", "bf16_gemv", "dequantize_rows", "moe_gate_up", "moe_down_combine",
+                 "nvfp4_unswizzle_scales", "w4a16_status_string", "w4a16_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+        assert name in _lib.SIGNATURES
+
+
+def test_status_strings():
+    lib = _lib.load()
+    assert lib.w4a16_status_string(OK) == b"ok"
+    assert lib.w4a16_status_string(UNSUPPORTED) == b"unsupported shape"
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: calls fail validation first
+
+
+def gemv(**kw):
+    a = dict(x=FAKE, M=1, K=4096, ldx=4096, w=FAKE, s=FAKE, gs=FAKE, N=4096, silu=0, out=FAKE)
+    a.update(kw)
+    return _lib.load().nvfp4_gemv(a["x"], a["M"], a["K"], a["ldx"], a["w"], a["s"], a["gs"], a["N"],
+                                  a["silu"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=33), UNSUPPORTED),
+    (dict(M=-1), INVALID),
+    (dict(K=4032 + 32), UNSUPPORTED),    # K % 64 != 0
+    (dict(K=0), INVALID),
+    (dict(N=4100), UNSUPPORTED),         # N % 16 != 0
+    (dict(N=0), INVALID),
+    (dict(N=48, silu=1), UNSUPPORTED),   # silu needs N % 32 == 0
+    (dict(silu=2), INVALID),
+    (dict(ldx=4000), INVALID),           # ldx < K
+    (dict(ldx=4100), MISALIGNED),        # ldx % 8 != 0
+    (dict(x=FAKE + 2), MISALIGNED),
+    (dict(w=FAKE + 8), MISALIGNED),
+    (dict(s=FAKE + 4), MISALIGNED),
+    (dict(gs=FAKE + 2), MISALIGNED),
+    (dict(out=FAKE + 1), MISALIGNED),
+    (dict(x=None), INVALID),
+    (dict(s=None), INVALID),
+    (dict(gs=None), INVALID),
+    (dict(M=0, x=None, w=None, s=None, gs=None, out=None), OK),  # M == 0: no-op
+])
+def test_nvfp4_gemv_argument_errors(kw, status):
+    assert gemv(**kw) == status
+    if status != OK:
+        assert _lib.load().w4a16_last_error()
+
+
+def test_bf16_gemv_argument_errors():
+    lib = _lib.load()
+    assert lib.bf16_gemv(FAKE, 33, 4096, 4096, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
+    assert lib.bf16_gemv(FAKE, 1, 4104, 4104, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED  # K % 16
+    assert lib.bf16_gemv(FAKE, 0, 4096, 4096, None, 4096, 0, None, None) == OK
+
+
+def test_dequantize_rows_argument_errors():
+    lib = _lib.load()
+    assert lib.dequantize_rows(FAKE, FAKE, 24, 4096, FAKE, None) == UNSUPPORTED  # rows % 16
+    assert lib.dequantize_rows(FAKE, FAKE, 32, 4160, FAKE, None) == UNSUPPORTED  # K % 256
+    assert lib.dequantize_rows(FAKE + 4, FAKE, 32, 4096, FAKE, None) == MISALIGNED
+    assert lib.dequantize_rows(None, FAKE, 32, 4096, FAKE, None) == INVALID
+    assert lib.dequantize_rows(None, None, 0, 4096, None, None) == OK
+
+
+def test_unswizzle_argument_errors():
+    lib = _lib.load()
+    assert lib.nvfp4_unswizzle_scales(FAKE, 16, 40, FAKE, None) == UNSUPPORTED
+    assert lib.nvfp4_unswizzle_scales(None, 16, 64, FAKE, None) == INVALID
+    assert lib.nvfp4_unswizzle_scales(None, 0, 64, None, None) == OK
+
+
+def test_moe_argument_errors():
+    lib = _lib.load()
+    gu = lambda **kw: lib.moe_gate_up(*[kw.get(k, v) for k, v in dict(
+        x=FAKE, M=1, H=4096, ids=FAKE, topk=8, E=128, w1=FAKE, s1=FAKE, alpha=FAKE, I=1536,
+        act=FAKE, wsh=FAKE, ssh=FAKE, gssh=FAKE, SI=1536, sact=FAKE, st=None).items()])
+    assert gu(M=33) == UNSUPPORTED
+    assert gu(topk=17) == UNSUPPORTED
+    assert gu(topk=0) == INVALID
+    assert gu(H=4000) == UNSUPPORTED
+    assert gu(I=1544 - 1) == UNSUPPORTED
+    assert gu(ids=None) == INVALID
+    assert gu(w1=FAKE + 4) == MISALIGNED
+    assert gu(M=0, x=None, ids=None) == OK
+    dc = lambda **kw: lib.moe_down_combine(*[kw.get(k, v) for k, v in dict(
+        act=FAKE, ids=FAKE, tw=FAKE, M=1, topk=8, E=128, w2=FAKE, s2=FAKE, alpha2=FAKE, H=4096,
+        I=1536, sact=FAKE, wsd=FAKE, ssd=FAKE, gssd=FAKE, SI=1536, out=FAKE, st=None).items()])
+    assert dc(I=1568) == UNSUPPORTED   # I % 64
+    assert dc(SI=1552) == UNSUPPORTED
+    assert dc(H=4104) == UNSUPPORTED   # H % 16
+    assert dc(tw=None) == INVALID
+    assert dc(act=FAKE + 8) == MISALIGNED
+    assert dc(M=0, act=None) == OK

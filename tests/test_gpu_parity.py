@@ -1,0 +1,273 @@
+"""GPU parity: every entry point, called through the C ABI (via the thin Python
+binding), against the binary64 CPU oracle on the same seeded host inputs.
+
+Bars: bit-exact for dequantize_rows and the scale un-swizzle; for the GEMVs
+one BF16 ulp of the oracle's binary64 value plus 1e-3 * sum|x*w| * |gs| (and
+the tighter bound any FP32 summation order meets); propagated bounds for the
+SiLU epilogues and the MoE combine (tests/helpers.py).  Full-size shapes are
+checked on whole 128-row bands sampled from the weight (a band is a
+contiguous slice of both the codes and the flat scale buffer).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4a16_nvfp4_gemv_amd as lib
+from helpers import (check_down, check_gemv, check_routed_act, check_silu, swizzle_by_reshape,
+                     to_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+    yield
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def bands(w, s, k, idx):
+    """Rows of the 128-row bands `idx` and the matching flat scale bytes."""
+    per = (k // 64) * 512
+    ws = torch.cat([w[128 * b:128 * (b + 1)] for b in idx]).contiguous()
+    ss = torch.cat([s[per * b:per * (b + 1)] for b in idx]).contiguous()
+    return ws, ss
+
+
+def rows_of_bands(idx):
+    return np.concatenate([np.arange(128 * b, 128 * (b + 1)) for b in idx])
+
+
+# ------------------------------------------------------------------ bit-exact
+@pytest.mark.parametrize("n,k", [(16, 64), (48, 208), (128, 4096), (130, 80), (256, 512), (4096, 4096)])
+def test_unswizzle_bit_exact(n, k):
+    _say("unswizzle", n, k)
+    g = torch.Generator().manual_seed(n + k)
+    flat = torch.randint(0, 256, (synth.flat_scale_bytes(n, k),), generator=g, dtype=torch.uint8)
+    got = lib.nvfp4_unswizzle_scales(dev(flat), n, k).cpu().numpy()
+    assert np.array_equal(got, oracle.unswizzle_scales(flat.numpy(), n, k))
+
+
+def test_dequantize_rows_every_code_scale_pair_bit_exact():
+    n, k = 16, 4096
+    codes = np.tile(np.arange(16, dtype=np.uint8), (n, k // 16))
+    w = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    logical = ((np.arange(k // 16)[None, :] + 16 * np.arange(n)[:, None]) % 256).astype(np.uint8)
+    flat = swizzle_by_reshape(logical, n, k)
+    _say("dequantize_rows all pairs")
+    got = to_bits(lib.dequantize_rows(dev(torch.from_numpy(w)), dev(torch.from_numpy(flat))).cpu())
+    want, _ = oracle.dequantize_rows(w, flat, n, k)
+    nan_scale = np.repeat((logical & 0x7F) == 0x7F, 16, axis=1)
+    assert np.array_equal(got[~nan_scale], want[~nan_scale])   # includes -0 bit patterns
+    assert ((got[nan_scale] & 0x7F80) == 0x7F80).all() and ((got[nan_scale] & 0x7F) != 0).all()
+
+
+@pytest.mark.parametrize("rows,k", [(16, 256), (48, 512), (272, 1536), (4096, 4096)])
+def test_dequantize_rows_random_bit_exact(rows, k):
+    _say("dequantize_rows", rows, k)
+    d = synth.dense_w4a16(1, rows, k, seed=rows + k)
+    got = to_bits(lib.dequantize_rows(dev(d["w"]), dev(d["s"])).cpu())
+    want, inexact = oracle.dequantize_rows(d["w"].numpy(), d["s"].numpy(), rows, k)
+    assert inexact == 0
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ NVFP4 GEMV
+def run_nvfp4(d, n, silu=False):
+    out = lib.nvfp4_gemv(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]), silu_mul=silu)
+    torch.cuda.synchronize()
+    return to_bits(out.cpu())
+
+
+SMALL_M = [1, 2, 3, 4, 5, 8, 16, 17, 32]
+SMALL_NK = [(256, 512), (48, 64), (144, 192), (400, 320), (128, 4096), (16, 1536)]
+
+
+@pytest.mark.parametrize("m", SMALL_M)
+@pytest.mark.parametrize("n,k", SMALL_NK)
+def test_nvfp4_gemv_small_shapes(m, n, k):
+    _say("nvfp4_gemv", m, n, k)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k)
+    got = run_nvfp4(d, n)
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
+@pytest.mark.parametrize("n,k", [(256, 512), (96, 128), (288, 256), (512, 1536)])
+def test_nvfp4_gemv_silu_small_shapes(m, n, k):
+    _say("nvfp4_gemv silu", m, n, k)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m) + n + k)
+    got = run_nvfp4(d, n, silu=True)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=True)
+    check_silu(got, want, acc, absacc, d["gs"][0], f"silu M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("n,k,variant", [(4096, 4096, 0), (6144, 4096, 1)])
+def test_nvfp4_gemv_dense_sweep_full_size(m, n, k, variant):
+    _say("nvfp4_gemv full", m, n, k)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, variant))
+    got = run_nvfp4(d, n)
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_nvfp4_gemv_gate_up_silu_full_size_sampled(m):
+    n, k = 2 * 14336, 4096
+    hb = (n // 2) // 128
+    _say("nvfp4_gemv silu full", m, n, k)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m))
+    got = run_nvfp4(d, n, silu=True)
+    picks = [0, 37, hb - 1]
+    ws, ss = bands(d["w"], d["s"], k, picks + [hb + b for b in picks])
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], ws, ss, float(d["gs"][0]), ws.shape[0], silu_mul=True)
+    cols = rows_of_bands(picks)
+    check_silu(got[:, cols], want, acc, absacc, d["gs"][0], f"silu full M={m}")
+
+
+def test_nvfp4_gemv_row_stride_and_zero_tokens():
+    m, n, k = 3, 256, 512
+    d = synth.dense_w4a16(m, n, k, seed=77)
+    wide = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    wide[:, :k] = d["x"]
+    xv = dev(wide)[:, :k]
+    assert xv.stride(0) == k + 64
+    out = to_bits(lib.nvfp4_gemv(xv, dev(d["w"]), dev(d["s"]), dev(d["gs"])).cpu())
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(out, acc, absacc, d["gs"][0], k, "strided x")
+    empty = lib.nvfp4_gemv(dev(d["x"][:0]), dev(d["w"]), dev(d["s"]), dev(d["gs"]))
+    assert tuple(empty.shape) == (0, n)
+
+
+def test_nvfp4_gemv_is_deterministic():
+    d = synth.dense_w4a16(8, 4096, 4096, seed=5)
+    a = run_nvfp4(d, 4096)
+    b = run_nvfp4(d, 4096)
+    assert np.array_equal(a, b)
+
+
+def test_nvfp4_gemv_rejects_bad_shapes():
+    d = synth.dense_w4a16(33, 256, 512, seed=1)
+    with pytest.raises(lib.W4A16Error):
+        lib.nvfp4_gemv(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]))
+
+
+# ------------------------------------------------------------------ BF16 GEMV
+def run_bf16(d, silu=False):
+    out = lib.bf16_gemv(dev(d["x"]), dev(d["w"]), silu_mul=silu)
+    torch.cuda.synchronize()
+    return to_bits(out.cpu())
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
+@pytest.mark.parametrize("n,k", [(48, 64), (256, 512), (144, 1040), (64, 4096)])
+def test_bf16_gemv_small_shapes(m, n, k):
+    _say("bf16_gemv", m, n, k)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + n + k)
+    got = run_bf16(d)
+    _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"])
+    check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 32])
+@pytest.mark.parametrize("n,k,variant", [(4096, 4096, 0), (4096, 14336, 1)])
+def test_bf16_gemv_full_size_sampled_rows(m, n, k, variant):
+    _say("bf16_gemv full", m, n, k)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m, variant))
+    got = run_bf16(d)
+    rows = np.r_[0:64, 2000:2064, n - 64:n]
+    _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"][rows].contiguous())
+    check_gemv(got[:, rows], acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 32])
+def test_bf16_gemv_silu(m):
+    n, k = 512, 1024
+    d = synth.dense_bf16(m, n, k, seed=900 + m)
+    got = run_bf16(d, silu=True)
+    want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=True)
+    check_silu(got, want, acc, absacc, 1.0, f"bf16 silu M={m}")
+
+
+# ------------------------------------------------------------------ MoE
+def moe_run(wts, tok, m, topk, inter, si, h):
+    x = dev(tok["x"])
+    ids = dev(tok["ids"])
+    act = torch.empty((m * topk, inter), dtype=torch.bfloat16, device=DEV)
+    sact = torch.empty((m, si), dtype=torch.bfloat16, device=DEV)
+    gw = {k: dev(v) for k, v in wts.items()}
+    lib.moe_gate_up(x, ids, gw["w1"], gw["w1_sf"], gw["alpha"], act, gw["wsh"], gw["ssh"], gw["gssh"], sact)
+    out = torch.empty((m, h), dtype=torch.bfloat16, device=DEV)
+    lib.moe_down_combine(act, ids, dev(tok["tw"]), gw["w2"], gw["w2_sf"], gw["alpha2"], sact, gw["wsd"],
+                         gw["ssd"], gw["gssd"], out)
+    torch.cuda.synchronize()
+    return act.cpu(), sact.cpu(), to_bits(out.cpu())
+
+
+def moe_check(wts, tok, act, sact, out, tokens, what):
+    """Stage-wise: gate_up against the oracle; down_combine against the oracle
+    fed with the GPU's own act / sact (so stage errors do not compound)."""
+    topk = tok["ids"].shape[1]
+    pairs = np.concatenate([np.arange(t * topk, (t + 1) * topk) for t in tokens])
+    ids = tok["ids"][tokens].contiguous()
+    r = oracle.moe_gate_up(tok["x"][tokens].contiguous(), ids, wts["w1"], wts["w1_sf"], wts["alpha"],
+                           wts["wsh"], wts["ssh"], wts["gssh"])
+    alpha_pp = wts["alpha"].numpy()[ids.numpy().reshape(-1)]
+    check_routed_act(to_bits(act[pairs]), r["act"], r["acc_r"], r["abs_r"], alpha_pp, what + " act")
+    check_silu(to_bits(sact[tokens]), r["sact"], r["acc_s"], r["abs_s"], wts["gssh"][0], what + " sact")
+    d = oracle.moe_down_combine(act[pairs].contiguous(), ids, tok["tw"][tokens].contiguous(), wts["w2"],
+                                wts["w2_sf"], wts["alpha2"], sact[tokens].contiguous(), wts["wsd"],
+                                wts["ssd"], wts["gssd"])
+    a2 = wts["alpha2"].numpy()[ids.numpy()]
+    check_down(out[tokens], d["out"], d["acc_r"], d["abs_r"], d["acc_s"], d["abs_s"],
+               tok["tw"][tokens].numpy(), a2, wts["gssd"][0], what + " out")
+
+
+@pytest.mark.parametrize("m,e,topk,h,inter,si", [
+    (1, 4, 2, 256, 128, 128),
+    (3, 6, 3, 128, 192, 64),      # I not a multiple of 128: unaligned up quad
+    (5, 8, 4, 512, 256, 320),
+    (32, 16, 8, 256, 128, 128),
+])
+def test_moe_small_shapes(m, e, topk, h, inter, si):
+    _say("moe", m, e, topk, h, inter, si)
+    wts = synth.moe_weights(e, h, inter, si, seed=300 + m)
+    tok = synth.moe_tokens(m, h, e, topk, seed=400 + m)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), f"moe M={m}")
+
+
+@pytest.fixture(scope="module")
+def moe_block_weights():
+    return synth.moe_weights(synth.MOE_EXPERTS, synth.MOE_HIDDEN, synth.MOE_INTER,
+                             synth.MOE_SHARED_INTER, seed=synth.seed_for(4, 0))
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_moe_decode_block_full_size(m, moe_block_weights):
+    _say("moe full", m)
+    wts = moe_block_weights
+    tok = synth.moe_tokens(m, synth.MOE_HIDDEN, synth.MOE_EXPERTS, synth.MOE_TOPK, seed=synth.seed_for(4, m))
+    act, sact, out = moe_run(wts, tok, m, synth.MOE_TOPK, synth.MOE_INTER, synth.MOE_SHARED_INTER,
+                             synth.MOE_HIDDEN)
+    tokens = list(range(m)) if m <= 2 else [0, m // 2, m - 1]
+    moe_check(wts, tok, act, sact, out, tokens, f"moe full M={m}")

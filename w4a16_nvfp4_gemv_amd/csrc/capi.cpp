@@ -1,0 +1,220 @@
+// C ABI of the library: argument validation, path choice and launch.
+// No entry point allocates memory, synchronizes or aborts; a call that
+// cannot run returns a non-zero status and enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <string>
+
+#include "../../include/w4a16_nvfp4_gemv.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, long long a = 0, long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, fmt, a, b);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return W4A16_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(e);
+  return W4A16_ERR_HIP;
+}
+
+int64_t flat_scale_bytes(int64_t n, int64_t k) {
+  return (n + 127) / 128 * 128 * ((k / 16 + 3) / 4 * 4);
+}
+
+// Checks shared by the dense GEMV entry points.  Returns W4A16_OK to go on.
+int check_dense(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const void* w, int64_t N,
+                int silu_mul, const uint16_t* out, int64_t k_multiple) {
+  if (M < 0 || K <= 0 || N <= 0 || ldx < K) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld N=%lld", M, N);
+  if (M > W4A16_MAX_M) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld exceeds the %lld-token limit", M, W4A16_MAX_M);
+  if (K > kMaxDim || N > kMaxDim || ldx > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large K=%lld N=%lld", K, N);
+  if (K % k_multiple) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of %lld", K, k_multiple);
+  if (N % 16) return fail(W4A16_ERR_UNSUPPORTED, "N=%lld is not a multiple of 16", N);
+  if (silu_mul != 0 && silu_mul != 1) return fail(W4A16_ERR_INVALID_ARG, "silu_mul=%lld must be 0 or 1", silu_mul);
+  if (silu_mul && N % 32) return fail(W4A16_ERR_UNSUPPORTED, "silu_mul needs N %% 32 == 0, N=%lld", N);
+  if (M == 0) return ok();
+  if (!x || !w || !out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(w, 16) || ldx % 8) return fail(W4A16_ERR_MISALIGNED, "x/w must be 16-byte aligned, ldx %% 8 == 0 (ldx=%lld)", ldx);
+  if (!aligned(out, 2)) return fail(W4A16_ERR_MISALIGNED, "out must be 2-byte aligned");
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported shape";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
+               const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
+               uint16_t* out, void* stream) {
+  int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 64);
+  if (st != W4A16_OK || M == 0) return st;
+  if (!w_scale || !global_scale) return fail(W4A16_ERR_INVALID_ARG, "null scale pointer");
+  if (!aligned(w_scale, 16) || !aligned(global_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w_scale must be 16-byte aligned");
+  w4a16::GemvParams p{};
+  p.x = x;
+  p.w = w;
+  p.s = w_scale;
+  p.gs = global_scale;
+  p.out = out;
+  p.ldx = ldx;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.half = silu_mul ? static_cast<int>(N / 2) : 0;
+  const int path = w4a16::choose_gemv_path(true, M, N, K);
+  return hip_status(w4a16::launch_gemv(true, p, silu_mul, path, static_cast<hipStream_t>(stream)));
+}
+
+int bf16_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w, int64_t N,
+              int silu_mul, uint16_t* out, void* stream) {
+  int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 16);
+  if (st != W4A16_OK || M == 0) return st;
+  w4a16::GemvParams p{};
+  p.x = x;
+  p.w = reinterpret_cast<const uint8_t*>(w);
+  p.s = nullptr;
+  p.gs = nullptr;
+  p.out = out;
+  p.ldx = ldx;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.half = silu_mul ? static_cast<int>(N / 2) : 0;
+  const int path = w4a16::choose_gemv_path(false, M, N, K);
+  return hip_status(w4a16::launch_gemv(false, p, silu_mul, path, static_cast<hipStream_t>(stream)));
+}
+
+int dequantize_rows(const uint8_t* w, const uint8_t* w_scale, int64_t rows, int64_t K,
+                    uint16_t* out, void* stream) {
+  if (rows < 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes rows=%lld K=%lld", rows, K);
+  if (rows % 16 || K % 256) return fail(W4A16_ERR_UNSUPPORTED, "needs rows %% 16 == 0 and K %% 256 == 0 (rows=%lld K=%lld)", rows, K);
+  if (rows > kMaxDim || K > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
+  if (rows == 0) return ok();
+  if (!w || !w_scale || !out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(w, 16) || !aligned(out, 16) || !aligned(w_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w/out 16-byte, w_scale 4-byte alignment required");
+  return hip_status(w4a16::launch_dequantize_rows(w, w_scale, rows, K, out, static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_unswizzle_scales(const uint8_t* w_scale, int64_t N, int64_t K, uint8_t* out,
+                           void* stream) {
+  if (N < 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes N=%lld K=%lld", N, K);
+  if (K % 16) return fail(W4A16_ERR_UNSUPPORTED, "K=%lld is not a multiple of 16", K);
+  if (N > kMaxDim || K > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
+  if (N == 0) return ok();
+  if (!w_scale || !out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  return hip_status(w4a16::launch_unswizzle(w_scale, N, K, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_gate_up(const uint16_t* x, int64_t M, int64_t H, const int32_t* ids, int64_t topk,
+                int64_t E, const uint8_t* w1, const uint8_t* w1_scale, const float* alpha,
+                int64_t I, uint16_t* act, const uint8_t* wsh, const uint8_t* ssh,
+                const float* gssh, int64_t SI, uint16_t* sact, void* stream) {
+  if (M < 0 || H <= 0 || topk <= 0 || E <= 0 || I <= 0 || SI <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld H=%lld", M, H);
+  if (M > W4A16_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
+  if (H % 64 || I % 16 || SI % 16) return fail(W4A16_ERR_UNSUPPORTED, "needs H %% 64, I %% 16, SI %% 16 == 0 (H=%lld I=%lld)", H, I);
+  if (H > kMaxDim || I > kMaxDim / 2 || SI > kMaxDim / 2 || E > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
+  if (M == 0) return ok();
+  if (!x || !ids || !w1 || !w1_scale || !alpha || !act || !wsh || !ssh || !gssh || !sact) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w1_scale, 16) || !aligned(wsh, 16) || !aligned(ssh, 16))
+    return fail(W4A16_ERR_MISALIGNED, "x, weights and scales must be 16-byte aligned");
+  if (!aligned(ids, 4) || !aligned(alpha, 4) || !aligned(gssh, 4) || !aligned(act, 2) || !aligned(sact, 2))
+    return fail(W4A16_ERR_MISALIGNED, "misaligned ids/alpha/outputs");
+  w4a16::MoeGateUpParams p{};
+  p.x = x;
+  p.ids = ids;
+  p.w1 = w1;
+  p.w1s = w1_scale;
+  p.alpha = alpha;
+  p.act = act;
+  p.wsh = wsh;
+  p.ssh = ssh;
+  p.gssh = gssh;
+  p.sact = sact;
+  p.w1_expert_bytes = 2 * I * (H / 2);
+  p.s1_expert_bytes = flat_scale_bytes(2 * I, H);
+  p.units_per_pair = (I + 127) / 128 * 32;
+  p.units_per_token = (SI + 127) / 128 * 32;
+  p.routed_units = M * topk * p.units_per_pair;
+  p.shared_units = M * p.units_per_token;
+  p.M = static_cast<int>(M);
+  p.H = static_cast<int>(H);
+  p.topk = static_cast<int>(topk);
+  p.E = static_cast<int>(E);
+  p.I = static_cast<int>(I);
+  p.SI = static_cast<int>(SI);
+  return hip_status(w4a16::launch_moe_gate_up(p, static_cast<hipStream_t>(stream)));
+}
+
+int moe_down_combine(const uint16_t* act, const int32_t* ids, const float* tw, int64_t M,
+                     int64_t topk, int64_t E, const uint8_t* w2, const uint8_t* w2_scale,
+                     const float* alpha2, int64_t H, int64_t I, const uint16_t* sact,
+                     const uint8_t* wsd, const uint8_t* ssd, const float* gssd, int64_t SI,
+                     uint16_t* out, void* stream) {
+  if (M < 0 || H <= 0 || topk <= 0 || E <= 0 || I <= 0 || SI <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld H=%lld", M, H);
+  if (M > W4A16_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
+  if (H % 16 || I % 64 || SI % 64) return fail(W4A16_ERR_UNSUPPORTED, "needs H %% 16, I %% 64, SI %% 64 == 0 (I=%lld SI=%lld)", I, SI);
+  if (H > kMaxDim || I > kMaxDim || SI > kMaxDim || E > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
+  if (M == 0) return ok();
+  if (!act || !ids || !tw || !w2 || !w2_scale || !alpha2 || !sact || !wsd || !ssd || !gssd || !out)
+    return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(act, 16) || !aligned(sact, 16) || !aligned(w2, 16) || !aligned(w2_scale, 16) || !aligned(wsd, 16) || !aligned(ssd, 16))
+    return fail(W4A16_ERR_MISALIGNED, "activations, weights and scales must be 16-byte aligned");
+  if (!aligned(ids, 4) || !aligned(tw, 4) || !aligned(alpha2, 4) || !aligned(gssd, 4) || !aligned(out, 2))
+    return fail(W4A16_ERR_MISALIGNED, "misaligned ids/tw/alpha2/out");
+  w4a16::MoeDownParams p{};
+  p.act = act;
+  p.ids = ids;
+  p.tw = tw;
+  p.w2 = w2;
+  p.w2s = w2_scale;
+  p.alpha2 = alpha2;
+  p.sact = sact;
+  p.wsd = wsd;
+  p.ssd = ssd;
+  p.gssd = gssd;
+  p.out = out;
+  p.w2_expert_bytes = H * (I / 2);
+  p.s2_expert_bytes = flat_scale_bytes(H, I);
+  p.units_per_token = (H + 127) / 128 * 32;
+  p.units = M * p.units_per_token;
+  p.M = static_cast<int>(M);
+  p.topk = static_cast<int>(topk);
+  p.E = static_cast<int>(E);
+  p.H = static_cast<int>(H);
+  p.I = static_cast<int>(I);
+  p.SI = static_cast<int>(SI);
+  return hip_status(w4a16::launch_moe_down_combine(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device-side building blocks shared by the gfx950 kernels: element decode,
+// 128x4 scale addressing, wave reductions and the XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- decode
+// FP8 E4M3FN byte `sel` of `word` -> f32.  gfx950's v_cvt_f32_fp8 decodes the
+// OCP E4M3FN format (bias 7, NaN at 0x7F/0xFF, no inf); every value is exact
+// in f32.
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), SEL);
+}
+
+// The two FP4 E2M1 codes of byte `SEL` of `word` (low nibble first) -> two
+// exact f32 values.  The hardware conversion takes only the exponent of its
+// scale operand, so it runs with scale 1 and the E4M3 block scale is applied
+// by an ordinary f32 multiply (e2m1 * e4m3 has at most 6 significant bits:
+// exact in f32 and in bf16).
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+// Two f32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Exactly dequantized weights of byte SEL of `word`, as a packed bf16 pair.
+template <int SEL>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t word, float scale) {
+  f32x2 f = e2m1x2_to_f32<SEL>(word);
+  return pack_bf16x2(f.x * scale, f.y * scale);
+}
+
+// Eight dequantized weights (one packed dword of codes) as bf16 pairs.
+__device__ __forceinline__ void dequant_dword(uint32_t word, float scale, uint32_t out[4]) {
+  out[0] = dequant_pair<0>(word, scale);
+  out[1] = dequant_pair<1>(word, scale);
+  out[2] = dequant_pair<2>(word, scale);
+  out[3] = dequant_pair<3>(word, scale);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  return static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+// a.x*b.x + a.y*b.y + c on packed bf16 pairs, FP32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// SiLU in FP32 with the accurate exponential and IEEE division.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g / (1.0f + expf(-g));
+}
+
+// ---------------------------------------------------------------- layout
+// The flat 128x4-swizzled scale buffer is a sequence of 512-byte tiles of
+// 128 rows x 4 scale columns (64 k), ordered by 128-row band then by column
+// group.  Row r of a band lives in the 16-byte chunk r % 32 at byte
+// (r / 32) * 4; the 4 bytes of that word are the 4 consecutive columns.
+// So the scale words of rows {r, r+32, r+64, r+96} for one 64-k tile are one
+// aligned 16-byte chunk: the "quad" the kernels are built around.
+__device__ __forceinline__ int64_t scale_chunk_offset(int64_t band, int64_t tile,
+                                                      int64_t tiles_per_row, int r32) {
+  return (band * tiles_per_row + tile) * 512 + r32 * 16;
+}
+
+__device__ __forceinline__ int64_t scale_word_offset(int64_t row, int64_t tile,
+                                                     int64_t tiles_per_row) {
+  int64_t band = row >> 7;
+  int r = static_cast<int>(row & 127);
+  return (band * tiles_per_row + tile) * 512 + (r & 31) * 16 + (r >> 5) * 4;
+}
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ uint32_t load4(const void* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// ---------------------------------------------------------------- reduce
+// Sum over aligned groups of G lanes (G a power of two <= 64); every lane of
+// the group ends up with the group sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- XCD order
+// Workgroups are dispatched round-robin over the 8 XCDs (hardware id b runs on
+// XCD b % 8).  Renumbering them so that consecutive logical ids share an XCD
+// keeps the blocks that read neighbouring scale chunks (and the same 128-byte
+// L2 lines) on one L2.
+__device__ __forceinline__ int xcd_logical_block() {
+  const int b = blockIdx.x, g = gridDim.x;
+  const int xcd = b & 7, idx = b >> 3;
+  const int q = g >> 3, rem = g & 7;
+  return xcd * q + (xcd < rem ? xcd : rem) + idx;
+}
+
+}  // namespace w4a16

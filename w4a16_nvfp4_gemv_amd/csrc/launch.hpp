@@ -1,0 +1,70 @@
+// Host-side interface between the C ABI (capi.cpp) and the kernel launchers.
+// Arguments reaching these launchers have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+constexpr int kPathValu = 0;
+constexpr int kPathMfma = 1;
+
+struct GemvParams {
+  const uint16_t* x;   // bf16 [M][ldx]
+  const uint8_t* w;    // packed codes [N][K/2] or bf16 [N][K] (as bytes)
+  const uint8_t* s;    // flat 128x4 scales (NVFP4), else unused
+  const float* gs;     // device FP32 global scale (NVFP4), else unused
+  uint16_t* out;       // bf16 [M][N] or [M][N/2]
+  int64_t ldx;
+  int64_t tiles;       // set by the launcher
+  int64_t units;       // set by the launcher
+  int M, N, K;
+  int half;            // N / 2 with silu_mul, else 0
+};
+
+int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream);
+
+hipError_t launch_dequantize_rows(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K,
+                                  uint16_t* out, hipStream_t stream);
+hipError_t launch_unswizzle(const uint8_t* s, int64_t N, int64_t K, uint8_t* out,
+                            hipStream_t stream);
+
+struct MoeGateUpParams {
+  const uint16_t* x;      // bf16 [M][H]
+  const int32_t* ids;     // [M][topk]
+  const uint8_t* w1;      // [E][2I][H/2]
+  const uint8_t* w1s;     // E flat buffers
+  const float* alpha;     // [E]
+  uint16_t* act;          // [M*topk][I]
+  const uint8_t* wsh;     // [2SI][H/2]
+  const uint8_t* ssh;
+  const float* gssh;      // [1]
+  uint16_t* sact;         // [M][SI]
+  int64_t w1_expert_bytes, s1_expert_bytes;
+  int64_t routed_units, shared_units, units_per_pair, units_per_token;
+  int M, H, topk, E, I, SI;
+};
+
+struct MoeDownParams {
+  const uint16_t* act;    // [M*topk][I]
+  const int32_t* ids;     // [M][topk]
+  const float* tw;        // [M][topk]
+  const uint8_t* w2;      // [E][H][I/2]
+  const uint8_t* w2s;
+  const float* alpha2;    // [E]
+  const uint16_t* sact;   // [M][SI]
+  const uint8_t* wsd;     // [H][SI/2]
+  const uint8_t* ssd;
+  const float* gssd;      // [1]
+  uint16_t* out;          // [M][H]
+  int64_t w2_expert_bytes, s2_expert_bytes;
+  int64_t units_per_token, units;
+  int M, topk, E, H, I, SI;
+};
+
+hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream);
+hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream);
+
+}  // namespace w4a16
