@@ -31,8 +31,14 @@
  *
  * Shape limits shared by the GEMV entry points: 0 <= M <= 32 tokens (M == 0
  * is a successful no-op), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
- * Pointer alignment: activations and weights 16 bytes, scales 4 bytes,
- * outputs 4 bytes; the row stride ldx of x is a multiple of 8 elements.
+ * Pointer alignment: activations, weights and scale buffers 16 bytes,
+ * global scale 4 bytes, outputs 2 bytes; the row stride ldx of x is a
+ * multiple of 8 elements.  Each of x, the weight and the scale buffer must
+ * span less than 2 GiB.
+ *
+ * The kernels read past-the-end rows and tiles through buffer resources that
+ * return zeros, so no entry point reads outside the extents given here; the
+ * results are deterministic (a fixed reduction order, no atomics).
  */
 #ifndef W4A16_NVFP4_GEMV_H
 #define W4A16_NVFP4_GEMV_H
@@ -75,7 +81,7 @@ int nvfp4_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
 /*
  * bf16_gemv -- the same GEMV with a row-major BF16 weight w [N][K] (device)
  * and a global scale of one (nvfp4_gemv page, function bf16_gemv).
- * Arguments and limits as nvfp4_gemv, except K % 8 == 0 suffices.
+ * Arguments and limits as nvfp4_gemv, except that K % 16 == 0 suffices.
  */
 int bf16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
               const uint16_t *w, int64_t N, int silu_mul, uint16_t *out, void *stream);

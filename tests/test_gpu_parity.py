@@ -100,30 +100,43 @@ SMALL_M = [1, 2, 3, 4, 5, 8, 16, 17, 32]
 SMALL_NK = [(256, 512), (48, 64), (144, 192), (400, 320), (128, 4096), (16, 1536)]
 
 
+PATHS = ["auto", "valu", "mfma"]
+
+
+@pytest.fixture
+def gemv_path(request, monkeypatch):
+    """Forces the kernel family (valu / mfma; valu only where it applies)."""
+    monkeypatch.setenv("W4A16_GEMV_PATH", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", SMALL_M)
 @pytest.mark.parametrize("n,k", SMALL_NK)
-def test_nvfp4_gemv_small_shapes(m, n, k):
-    _say("nvfp4_gemv", m, n, k)
+def test_nvfp4_gemv_small_shapes(m, n, k, gemv_path):
+    _say("nvfp4_gemv", m, n, k, gemv_path)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k)
     got = run_nvfp4(d, n)
     _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
 @pytest.mark.parametrize("n,k", [(256, 512), (96, 128), (288, 256), (512, 1536)])
-def test_nvfp4_gemv_silu_small_shapes(m, n, k):
-    _say("nvfp4_gemv silu", m, n, k)
+def test_nvfp4_gemv_silu_small_shapes(m, n, k, gemv_path):
+    _say("nvfp4_gemv silu", m, n, k, gemv_path)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m) + n + k)
     got = run_nvfp4(d, n, silu=True)
     want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=True)
     check_silu(got, want, acc, absacc, d["gs"][0], f"silu M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
 @pytest.mark.parametrize("n,k,variant", [(4096, 4096, 0), (6144, 4096, 1)])
-def test_nvfp4_gemv_dense_sweep_full_size(m, n, k, variant):
-    _say("nvfp4_gemv full", m, n, k)
+def test_nvfp4_gemv_dense_sweep_full_size(m, n, k, variant, gemv_path):
+    _say("nvfp4_gemv full", m, n, k, gemv_path)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, variant))
     got = run_nvfp4(d, n)
     _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
@@ -158,11 +171,13 @@ def test_nvfp4_gemv_row_stride_and_zero_tokens():
     assert tuple(empty.shape) == (0, n)
 
 
-def test_nvfp4_gemv_is_deterministic():
-    d = synth.dense_w4a16(8, 4096, 4096, seed=5)
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_nvfp4_gemv_is_deterministic(m):
+    """Split-K partials are added in split order, so repeated calls agree bit for bit."""
+    d = synth.dense_w4a16(m, 4096, 4096, seed=5)
     a = run_nvfp4(d, 4096)
-    b = run_nvfp4(d, 4096)
-    assert np.array_equal(a, b)
+    for _ in range(3):
+        assert np.array_equal(a, run_nvfp4(d, 4096))
 
 
 def test_nvfp4_gemv_rejects_bad_shapes():
@@ -178,10 +193,11 @@ def run_bf16(d, silu=False):
     return to_bits(out.cpu())
 
 
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
-@pytest.mark.parametrize("n,k", [(48, 64), (256, 512), (144, 1040), (64, 4096)])
-def test_bf16_gemv_small_shapes(m, n, k):
-    _say("bf16_gemv", m, n, k)
+@pytest.mark.parametrize("n,k", [(48, 64), (256, 512), (144, 1040), (64, 4096), (32, 336)])
+def test_bf16_gemv_small_shapes(m, n, k, gemv_path):
+    _say("bf16_gemv", m, n, k, gemv_path)
     d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + n + k)
     got = run_bf16(d)
     _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"])
@@ -199,8 +215,9 @@ def test_bf16_gemv_full_size_sampled_rows(m, n, k, variant):
     check_gemv(got[:, rows], acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 3, 8, 32])
-def test_bf16_gemv_silu(m):
+def test_bf16_gemv_silu(m, gemv_path):
     n, k = 512, 1024
     d = synth.dense_bf16(m, n, k, seed=900 + m)
     got = run_bf16(d, silu=True)

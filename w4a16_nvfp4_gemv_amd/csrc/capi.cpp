@@ -81,11 +81,17 @@ int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8
   if (st != W4A16_OK || M == 0) return st;
   if (!w_scale || !global_scale) return fail(W4A16_ERR_INVALID_ARG, "null scale pointer");
   if (!aligned(w_scale, 16) || !aligned(global_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w_scale must be 16-byte aligned");
+  const int64_t w_bytes = N * (K / 2), s_bytes = flat_scale_bytes(N, K), x_bytes = ((M - 1) * ldx + K) * 2;
+  if (w_bytes > kMaxDim || s_bytes > kMaxDim || x_bytes > kMaxDim)
+    return fail(W4A16_ERR_UNSUPPORTED, "tensors above 2 GiB are not supported (weight %lld bytes)", w_bytes);
   w4a16::GemvParams p{};
   p.x = x;
   p.w = w;
   p.s = w_scale;
   p.gs = global_scale;
+  p.x_bytes = static_cast<uint32_t>(x_bytes);
+  p.w_bytes = static_cast<uint32_t>(w_bytes);
+  p.s_bytes = static_cast<uint32_t>(s_bytes);
   p.out = out;
   p.ldx = ldx;
   p.M = static_cast<int>(M);
@@ -100,11 +106,17 @@ int bf16_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16
               int silu_mul, uint16_t* out, void* stream) {
   int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 16);
   if (st != W4A16_OK || M == 0) return st;
+  const int64_t w_bytes = N * K * 2, x_bytes = ((M - 1) * ldx + K) * 2;
+  if (w_bytes > kMaxDim || x_bytes > kMaxDim)
+    return fail(W4A16_ERR_UNSUPPORTED, "tensors above 2 GiB are not supported (weight %lld bytes)", w_bytes);
   w4a16::GemvParams p{};
   p.x = x;
   p.w = reinterpret_cast<const uint8_t*>(w);
   p.s = nullptr;
   p.gs = nullptr;
+  p.x_bytes = static_cast<uint32_t>(x_bytes);
+  p.w_bytes = static_cast<uint32_t>(w_bytes);
+  p.s_bytes = 0;
   p.out = out;
   p.ldx = ldx;
   p.M = static_cast<int>(M);

@@ -95,6 +95,30 @@ __device__ __forceinline__ int64_t scale_word_offset(int64_t row, int64_t tile,
 }
 
 // ---------------------------------------------------------------- loads
+// Buffer-resource loads.  A load whose byte range reaches past the resource's
+// size returns zeros (per dword) instead of touching memory, so rows or tiles
+// past the end of a matrix are read as zeros without a branch: every load of
+// a wave can be issued back to back and waited for in order.  Offsets are
+// 32-bit, so one resource spans less than 2 GiB; kOutOfRange is an offset no
+// resource reaches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+// Streaming variant (non-temporal: the weights are read exactly once).
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -106,12 +130,24 @@ __device__ __forceinline__ uint32_t load4(const void* p) {
 }
 
 // ---------------------------------------------------------------- reduce
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64); every lane of
-// the group ends up with the group sum.
+// the group ends up with the group sum.  Inside a row of 16 lanes the partner
+// values come from DPP (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror: after each step every lane holds the sum of its 2, 4, 8, 16
+// lanes); the 16- and 32-lane steps use cross-lane shuffles.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  if constexpr (G >= 2) v += dpp_f32<0xB1>(v);
+  if constexpr (G >= 4) v += dpp_f32<0x4E>(v);
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

@@ -11,6 +11,9 @@
 // Both stream every weight byte exactly once with 16-byte loads, and both
 // apply the FP32 global scale to the FP32 sum before the single BF16 rounding
 // (nvfp4_gemv page, module docstring "Numerics").
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "unit_core.hpp"
@@ -18,59 +21,186 @@
 namespace w4a16 {
 
 // ------------------------------------------------------------------ VALU
+// A unit is a quad of rows (NVFP4) or 4 consecutive rows (BF16), plus the
+// matching up rows with silu_mul; LPQ lanes split the unit's K tiles.  The
+// workgroup first stages all M activation rows in LDS (their global loads are
+// issued before any weight load, so waiting for them never waits behind the
+// HBM stream), and every wave streams its (unit, tile) items with the next
+// item's loads in flight while the current one is computed.
+template <int R>
+struct UnitRows {
+  int64_t rows[R];
+  bool rv[R];
+  bool quad_ok[R / 4];
+};
+
+template <bool FP4, bool SILU, int R>
+__device__ __forceinline__ UnitRows<R> unit_rows(const GemvParams& p, int64_t u) {
+  UnitRows<R> r;
+  const int64_t limit = SILU ? p.half : p.N;
+  if constexpr (FP4) quad_rows<R>(u, limit, p.half, r.rows, r.rv);
+  else consecutive_rows<R>(u, limit, p.half, r.rows, r.rv);
+  if (u >= p.units) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.rv[i] = false;
+  }
+  r.quad_ok[0] = true;
+  if constexpr (R == 8) r.quad_ok[1] = FP4 && (p.half % 128 == 0);
+  return r;
+}
+
+// Index (in 16-byte chunks) of the spare LDS chunk that absorbs the writes of
+// staging slots past the end of the activations.
+__device__ __forceinline__ uint32_t chunks_dummy(int M, uint32_t xstride) {
+  return static_cast<uint32_t>(M) * (xstride / 8);
+}
+
 template <bool FP4, int MT, int LPQ, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
   constexpr int R = SILU ? 8 : 4;
   constexpr int G = kWave / LPQ;  // units a wave works on at once
-  const int lane = threadIdx.x & 63;
+  constexpr int XR = 8;           // 16-byte x chunks per thread issued before the weights
+  extern __shared__ u32x4 xs_raw[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xs_raw);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int li = lane % LPQ;
   const int slot = lane / LPQ;
-  const int wave = threadIdx.x >> 6;
-  const int64_t gwave = static_cast<int64_t>(xcd_logical_block()) * 4 + wave;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4 * G;
-  const int64_t limit = SILU ? p.half : p.N;
-  const int64_t row_bytes = FP4 ? p.K / 2 : static_cast<int64_t>(p.K) * 2;
-  const float gs = FP4 ? *p.gs : 1.0f;
-  const bool quad_b = FP4 && SILU && (p.half % 128 == 0);
+  // 32-bit bookkeeping: units, tiles and items all stay far below 2^31
+  const int nwaves = static_cast<int>(gridDim.x) * 4;
+  const int gwave = xcd_logical_block() * 4 + (tid >> 6);
+  const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
+  const uint32_t xstride = (p.K + 63) / 64 * 64;  // LDS row stride (elements)
+  const int tiles = static_cast<int>(p.tiles);
+  const int units = static_cast<int>(p.units);
+  const int ntl = (tiles + LPQ - 1) / LPQ;  // tiles per lane per unit
+  const int first = gwave * G;
+  const int nbatch = first < units ? (units - first + nwaves * G - 1) / (nwaves * G) : 0;
+  const int n_items = nbatch * ntl;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
 
-  for (int64_t ubase = gwave * G; ubase < p.units; ubase += stride) {
-    const int64_t u = ubase + slot;
-    const bool active = u < p.units;
-    int64_t rows[R];
-    bool rv[R];
-    if constexpr (FP4) quad_rows<R>(u, limit, p.half, rows, rv);
-    else consecutive_rows<R>(u, limit, p.half, rows, rv);
-    bool quad_ok[R / 4];
-    quad_ok[0] = true;
-    if constexpr (R == 8) quad_ok[1] = quad_b;
-    float acc[R][MT];
-    unit_dot<FP4, R, MT, LPQ>(p.w, row_bytes, p.s, p.tiles, rows, rv, quad_ok, p.x, p.ldx,
-                              p.M, li, active, acc);
-    if (!active) continue;
-    // Each lane of the group writes the outputs whose index is li mod LPQ.
+  // 1. activations: the first XR chunks of every thread, before any weight load
+  const uint32_t kc = p.K / 8;
+  const uint32_t chunks = static_cast<uint32_t>(p.M) * kc;
+  u32x4 xv[XR];
+  uint32_t xdst[XR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const uint32_t c = r * 256 + tid;
+    const uint32_t m = c / kc, q = c - m * kc;
+    const bool ok = c < chunks;
+    xv[r] = bload16(rx, ok ? m * static_cast<uint32_t>(p.ldx) * 2 + q * 16 : kOutOfRange);
+    xdst[r] = ok ? m * (xstride / 8) + static_cast<uint32_t>(lds_chunk(q)) : chunks_dummy(p.M, xstride);
+  }
+
+  // 2. first item's weight loads
+  TileRegs<R> A, B;
+  UnitRows<R> ua, ub;
+  bool ta = false, tb = false;
+  uint32_t tA = 0, tB = 0;
+  // (issued unconditionally -- a wave without items reads out of range, i.e.
+  // nothing -- so that no branch separates these loads from the x loads)
+  ua = unit_rows<FP4, SILU, R>(p, first + slot);
+  tA = li;
+  ta = n_items > 0 && static_cast<int>(tA) < tiles;
+  tile_issue<FP4, R>(A, rw, row_bytes, rs, p.tiles, ua.rows, ua.rv, ua.quad_ok, tA, ta);
+
+  // 3. activations into LDS (swizzled 16-byte chunks; unused slots write a dummy chunk)
+  u32x4* xs4 = reinterpret_cast<u32x4*>(xs);
+#pragma unroll
+  for (int r = 0; r < XR; ++r) xs4[xdst[r]] = xv[r];
+  for (uint32_t c = XR * 256 + tid; c < chunks; c += 256) {
+    const uint32_t m = c / kc, q = c - m * kc;
+    xs4[m * (xstride / 8) + lds_chunk(q)] = bload16(rx, m * static_cast<uint32_t>(p.ldx) * 2 + q * 16);
+  }
+  __syncthreads();
+
+  const float gs = FP4 ? *p.gs : 1.0f;
+  float acc[R][MT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+
+  auto finish_unit = [&](const UnitRows<R>& ur) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[i][m] = group_sum<LPQ>(acc[i][m]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if ((i * MT + m) % LPQ != li || m >= p.M || !rv[i]) continue;
-        if constexpr (!SILU) {
-          p.out[m * static_cast<int64_t>(p.N) + rows[i]] = f32_to_bf16_bits(acc[i][m] * gs);
-        } else {
-          const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][m] * gs));
-          const float up = bf16_bits_to_f32(f32_to_bf16_bits(acc[4 + i][m] * gs));
-          p.out[m * static_cast<int64_t>(p.half) + rows[i]] = f32_to_bf16_bits(silu_f32(g) * up);
+        if ((i * MT + m) % LPQ == li && m < p.M && ur.rv[i]) {
+          if constexpr (!SILU) {
+            p.out[m * static_cast<int64_t>(p.N) + ur.rows[i]] = f32_to_bf16_bits(acc[i][m] * gs);
+          } else {
+            const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][m] * gs));
+            const float up = bf16_bits_to_f32(f32_to_bf16_bits(acc[4 + i][m] * gs));
+            p.out[m * static_cast<int64_t>(p.half) + ur.rows[i]] = f32_to_bf16_bits(silu_f32(g) * up);
+          }
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+  };
+
+  // Items run unit batch by unit batch, tile by tile: (ub, tj) is the item
+  // held in buffer B next, advanced without divisions.
+  int nb_unit = first + slot, nb_tj = 0;
+  auto advance = [&]() {
+    if (++nb_tj == ntl) {
+      nb_tj = 0;
+      nb_unit += nwaves * G;
+    }
+  };
+  advance();  // item 0 is already in A
+  for (int it = 0; it < n_items; it += 2) {
+    // A holds item it; bring item it+1 into B
+    if (it + 1 < n_items) {
+      ub = unit_rows<FP4, SILU, R>(p, nb_unit);
+      tB = static_cast<uint32_t>(li + nb_tj * LPQ);
+      tb = static_cast<int>(tB) < tiles;
+      tile_issue<FP4, R>(B, rw, row_bytes, rs, p.tiles, ub.rows, ub.rv, ub.quad_ok, tB, tb);
+      advance();
+    }
+    tile_compute<FP4, R, MT>(A, xs, xstride, tA, p.M, ta && ua.rv[0], acc);
+    if ((it % ntl) == ntl - 1) finish_unit(ua);
+    if (it + 1 >= n_items) break;
+    // B holds item it+1; bring item it+2 into A
+    if (it + 2 < n_items) {
+      ua = unit_rows<FP4, SILU, R>(p, nb_unit);
+      tA = static_cast<uint32_t>(li + nb_tj * LPQ);
+      ta = static_cast<int>(tA) < tiles;
+      tile_issue<FP4, R>(A, rw, row_bytes, rs, p.tiles, ua.rows, ua.rv, ua.quad_ok, tA, ta);
+      advance();
+    }
+    tile_compute<FP4, R, MT>(B, xs, xstride, tB, p.M, tb && ub.rv[0], acc);
+    if (((it + 1) % ntl) == ntl - 1) finish_unit(ub);
   }
 }
 
 // ------------------------------------------------------------------ MFMA
-// Tile of 16 rows: NVFP4 rows {band*128 + 4q + (r&3) + 32(r>>2)} (q = tile % 8),
-// whose scale words for one 64-k tile are 64 contiguous bytes; BF16 rows are
-// 16 consecutive rows.  A step covers 128 k (NVFP4: 64 bytes per row, one
-// 16-byte load per lane feeding 4 MFMAs) or 32 k (BF16: one 16-byte load per
-// lane feeding 1 MFMA).  Lane l supplies row l%16 and k-group l/16.
+// Swap-AB MFMA path.  A row tile is 16 weight rows, the A operand of
+// v_mfma_f32_16x16x32_bf16; the B operand holds up to 16 tokens (two token
+// tiles for M > 16).  NVFP4 tile rows are {band*128 + 4q + (r&3) + 32(r>>2)}
+// (q = tile % 8): their scale words for a 64-k tile are 64 contiguous bytes.
+// BF16 tile rows are 16 consecutive rows.
+//
+// One workgroup per row tile (plus the matching up tile with silu_mul); its
+// four waves split K into contiguous quarters and meet in LDS at the end.  A
+// step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes feeding 4
+// MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights feeding 1
+// MFMA).  Each wave keeps D steps in flight in a ring: for every step the B
+// fragments (read straight from x) are issued before the weights, so the
+// in-order wait for a step's x never waits behind the HBM stream, and every
+// ring iteration issues the same loads (steps past the wave's share read
+// zeros through out-of-range offsets), which keeps the waits exact.
 template <bool FP4>
 __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
   if constexpr (FP4) return (tile >> 3) * 128 + (tile & 7) * 4 + (r & 3) + 32 * (r >> 2);
@@ -79,17 +209,26 @@ __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
 
 template <bool FP4, int NT, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
-  constexpr int NA = SILU ? 2 : 1;           // A operands per step (gate, up)
-  constexpr int KSTEP = FP4 ? 128 : 32;       // k per step
-  __shared__ f32x4 red[4][NA][NT][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int NA = SILU ? 2 : 1;          // A operands per step (gate, up)
+  constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
+  constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
+  constexpr int D = FP4 ? (NT == 1 ? 8 : 4) : (NT == 1 ? 16 : 8);  // steps in flight
+  __shared__ f32x4 red[3][NA][NT][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int64_t limit = SILU ? p.half : p.N;
-  const int64_t row_bytes = FP4 ? p.K / 2 : static_cast<int64_t>(p.K) * 2;
+  const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
+  const int64_t steps_total = (p.K + KSTEP - 1) / KSTEP;
+  const int64_t spw = (steps_total + 3) / 4;           // steps per wave
+  const int64_t st0 = wave * spw;
+  const int64_t nst = st0 < steps_total ? (steps_total - st0 < spw ? steps_total - st0 : spw) : 0;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   const float gs = FP4 ? *p.gs : 1.0f;
-  const int64_t nsteps = (p.K + KSTEP - 1) / KSTEP;
 
   for (int64_t tile = xcd_logical_block(); tile < p.units; tile += gridDim.x) {
     int64_t rows[NA];
@@ -100,91 +239,110 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
       rows[1] = rows[0] + p.half;
       rv[1] = rv[0];
     }
+    // x offsets of this lane's B fragments: token 16n + r (bytes), zero past M
+    uint32_t xo[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int m = 16 * n + r;
+      xo[n] = m < p.M ? static_cast<uint32_t>(m) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
+    }
+    u32x4 xb[D][NJ][NT];
+    u32x4 wb[D][NA];
+    uint32_t sb[D][NA];
+    auto issue = [&](int d, int64_t st) {
+      const bool sv = st < nst;
+      const uint32_t kb = static_cast<uint32_t>((st0 + st) * KSTEP);  // first k of the step
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t k = kb + (FP4 ? g * 32 + 8 * j : g * 8);
+        const bool ok = sv && k < static_cast<uint32_t>(p.K);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xb[d][j][n] = bload16(rx, ok ? xo[n] + k * 2 : kOutOfRange);
+      }
+      const uint32_t k = kb + (FP4 ? g * 32 : g * 8);
+      const bool kv = sv && k < static_cast<uint32_t>(p.K);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const bool ok = rv[a] && kv;
+        if constexpr (FP4) {
+          sb[d][a] = bload4(rs, ok ? static_cast<uint32_t>(scale_word_offset(rows[a], k / 64, p.tiles)) : kOutOfRange);
+          wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k / 2 : kOutOfRange);
+        } else {
+          sb[d][a] = 0;
+          wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k * 2 : kOutOfRange);
+        }
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, d);
+
     f32x4 acc[NA][NT];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
 
-    for (int64_t st = wave; st < nsteps; st += 4) {
-      if constexpr (FP4) {
-        const int64_t k0 = st * 128 + g * 32;  // this lane's 32 k
-        const bool kv = k0 < p.K;
-        u32x4 wv[NA];
-        uint32_t sw[NA];
+    for (int64_t base = 0; base < nst; base += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        u32x4 xc[NJ][NT];
+        u32x4 wc[NA];
+        uint32_t sc[NA];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) xc[j][n] = xb[d][j][n];
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-          if (rv[a] && kv) {
-            wv[a] = load16_nt(p.w + rows[a] * row_bytes + k0 / 2);
-            sw[a] = load4(p.s + scale_word_offset(rows[a], k0 / 64, p.tiles)) >> (16 * (g & 1));
-          } else {
-            wv[a] = u32x4{0, 0, 0, 0};
-            sw[a] = 0;
-          }
+          wc[a] = wb[d][a];
+          sc[a] = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
         }
+        issue(d, base + d + D);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // B fragments: tokens 16n + r, k0 + 8j .. +7
-          bf16x8 bx[NT];
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            const int m = 16 * n + r;
-            u32x4 v = (m < p.M && kv) ? load16(p.x + m * p.ldx + k0 + 8 * j) : u32x4{0, 0, 0, 0};
-            bx[n] = __builtin_bit_cast(bf16x8, v);
-          }
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int a = 0; a < NA; ++a) {
-            const float sc = (j < 2) ? e4m3_to_f32<0>(sw[a]) : e4m3_to_f32<1>(sw[a]);
-            const uint32_t word = (j == 0) ? wv[a].x : (j == 1) ? wv[a].y : (j == 2) ? wv[a].z : wv[a].w;
-            uint32_t pr[4];
-            dequant_dword(word, sc, pr);
-            const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+            bf16x8 av;
+            if constexpr (FP4) {
+              const float scale = (j < 2) ? e4m3_to_f32<0>(sc[a]) : e4m3_to_f32<1>(sc[a]);
+              const uint32_t word = (j == 0) ? wc[a].x : (j == 1) ? wc[a].y : (j == 2) ? wc[a].z : wc[a].w;
+              uint32_t pr[4];
+              dequant_dword(word, scale, pr);
+              av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+            } else {
+              av = __builtin_bit_cast(bf16x8, wc[a]);
+            }
 #pragma unroll
             for (int n = 0; n < NT; ++n)
-              acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[n], acc[a][n], 0, 0, 0);
+              acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xc[j][n]),
+                                                                  acc[a][n], 0, 0, 0);
           }
-        }
-      } else {
-        const int64_t k0 = st * 32 + g * 8;
-        const bool kv = k0 < p.K;
-        bf16x8 av[NA];
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          u32x4 v = (rv[a] && kv) ? load16_nt(p.w + rows[a] * row_bytes + k0 * 2) : u32x4{0, 0, 0, 0};
-          av[a] = __builtin_bit_cast(bf16x8, v);
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int m = 16 * n + r;
-          u32x4 v = (m < p.M && kv) ? load16(p.x + m * p.ldx + k0) : u32x4{0, 0, 0, 0};
-          const bf16x8 bx = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-          for (int a = 0; a < NA; ++a)
-            acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[a], bx, acc[a][n], 0, 0, 0);
         }
       }
     }
-    // Split-K reduction of the four waves through LDS.
+
+    // Four K quarters meet in LDS; wave 0 adds them (quarter order) and writes.
+    if (wave > 0) {
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) red[wave][a][n][lane] = acc[a][n];
+        for (int n = 0; n < NT; ++n) red[wave - 1][a][n][lane] = acc[a][n];
+    }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-          acc[a][n] = red[0][a][n][lane] + red[1][a][n][lane] + red[2][a][n][lane] + red[3][a][n][lane];
-      // C layout: lane l holds rows 4(l/16)+i of the tile, token column l%16.
+          acc[a][n] = ((acc[a][n] + red[0][a][n][lane]) + red[1][a][n][lane]) + red[2][a][n][lane];
+      // C layout: lane holds rows 4(l/16)+i of the tile, token column l%16
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const int m = 16 * n + (lane & 15);
-        if (m >= p.M) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t row = mfma_row<FP4>(tile, 4 * (lane >> 4) + i);
-          if (row >= limit) continue;
+          if (m >= p.M || row >= limit) continue;
           if constexpr (!SILU) {
             p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(acc[0][n][i] * gs);
           } else {
@@ -214,23 +372,26 @@ hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
   const int64_t g = kWave / lpq;
   const int64_t waves = (p.units + g - 1) / g;
   int64_t blocks = (waves + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 1024) blocks = 1024;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const size_t lds = static_cast<size_t>(p.M) * ((p.K + 63) / 64 * 64) * 2 + 16;  // + spare chunk
   switch (lpq) {
-    case 64: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 64, SILU>), grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 32, SILU>), grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 16, SILU>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 8, SILU>), grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 64, SILU>), grid, block, lds, stream, p); break;
+    case 32: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 32, SILU>), grid, block, lds, stream, p); break;
+    case 16: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 16, SILU>), grid, block, lds, stream, p); break;
+    default: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 8, SILU>), grid, block, lds, stream, p); break;
   }
   return hipGetLastError();
 }
 
 template <bool FP4, int NT, bool SILU>
-hipError_t launch_mfma(const GemvParams& p, hipStream_t stream) {
+hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
+  const int64_t limit = SILU ? p.half : p.N;
+  p.units = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   int64_t blocks = p.units;
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)), dim3(256),
-                     0, stream, p);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -246,18 +407,25 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
     return launch_valu<FP4, 4, SILU>(p, lpq, stream);
   }
   p.tiles = p.K / 64;
-  p.units = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   if (p.M <= 16) return launch_mfma<FP4, 1, SILU>(p, stream);
   return launch_mfma<FP4, 2, SILU>(p, stream);
 }
 
 }  // namespace
 
+// VALU dot path while the activations fit the 64 KB staging area and the
+// per-weight VALU work (about 0.5 + 0.5 M instructions) stays below the MFMA
+// path's dequantization cost; MFMA otherwise.  W4A16_GEMV_PATH=valu|mfma
+// forces a path (the tests use it to cover both at every M).
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K) {
-  (void)fp4;
   (void)N;
-  (void)K;
-  return M <= 4 ? kPathValu : kPathMfma;
+  const bool valu_fits = M <= 4 && M * ((K + 63) / 64 * 64) * 2 <= 65536;
+  if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
+    if (std::strcmp(env, "mfma") == 0) return kPathMfma;
+    if (std::strcmp(env, "valu") == 0 && valu_fits) return kPathValu;
+  }
+  const int64_t valu_max_m = fp4 ? 2 : 1;
+  return (valu_fits && M <= valu_max_m) ? kPathValu : kPathMfma;
 }
 
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream) {

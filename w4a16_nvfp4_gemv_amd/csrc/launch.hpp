@@ -19,6 +19,9 @@ struct GemvParams {
   int64_t ldx;
   int64_t tiles;       // set by the launcher
   int64_t units;       // set by the launcher
+  uint32_t x_bytes;     // byte extents of x, w and s (each below 2 GiB): the
+  uint32_t w_bytes;     // kernels read them through buffer resources whose
+  uint32_t s_bytes;     // out-of-range loads return zero
   int M, N, K;
   int half;            // N / 2 with silu_mul, else 0
 };

@@ -185,3 +185,146 @@ __device__ __forceinline__ void consecutive_rows(int64_t u, int64_t limit, int64
 }
 
 }  // namespace w4a16
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// Register-staged tile of one unit for the pipelined dense VALU kernel.
+template <int R>
+struct TileRegs {
+  u32x4 w[R][2];   // 32 bytes per row
+  uint32_t s[R];   // NVFP4 scale word per row (4 blocks of 16 k)
+};
+
+// Issues the loads of one (unit, tile) item: scale words first, then the rows
+// in order, so that a row's compute can start when its own loads land.  All
+// loads are unconditional buffer loads; rows that are not valid (past the
+// matrix, inactive unit, tile past K) use an out-of-range offset and read 0.
+template <bool FP4, int R>
+__device__ __forceinline__ void tile_issue(TileRegs<R>& b, rsrc_t w, uint32_t row_bytes, rsrc_t s,
+                                           uint32_t tiles_per_row, const int64_t (&rows)[R],
+                                           const bool (&rv)[R], const bool (&quad_ok)[R / 4],
+                                           uint32_t t, bool tv) {
+  if constexpr (FP4) {
+#pragma unroll
+    for (int h = 0; h < R / 4; ++h) {
+      if (quad_ok[h]) {
+        const uint32_t off = (tv && rv[4 * h])
+                                 ? static_cast<uint32_t>(scale_word_offset(rows[4 * h], t, tiles_per_row))
+                                 : kOutOfRange;
+        const u32x4 c = bload16(s, off);
+        b.s[4 * h + 0] = c.x;
+        b.s[4 * h + 1] = c.y;
+        b.s[4 * h + 2] = c.z;
+        b.s[4 * h + 3] = c.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t off = (tv && rv[4 * h + j])
+                                   ? static_cast<uint32_t>(scale_word_offset(rows[4 * h + j], t, tiles_per_row))
+                                   : kOutOfRange;
+          b.s[4 * h + j] = bload4(s, off);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const uint32_t off = (tv && rv[i]) ? static_cast<uint32_t>(rows[i]) * row_bytes + t * 32 : kOutOfRange;
+    b.w[i][0] = bload16_nt(w, off);
+    b.w[i][1] = bload16_nt(w, off + 16);
+  }
+}
+
+// Position of 16-byte chunk q of a staged activation row in LDS.  Lanes read
+// chunks 8 (NVFP4) or 2 (BF16) apart; XOR-ing the low 3 bits with bits 4..6
+// spreads 16 consecutive lanes over all 16 bank groups.
+__device__ __forceinline__ int64_t lds_chunk(int64_t q) { return q ^ ((q >> 4) & 7); }
+
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_bf16(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL));
+}
+
+// Accumulates one staged tile.  x comes from LDS: xs points at token 0 of the
+// staged activations, xstride elements per token.
+//   NVFP4 (64 k): per 16-k block, the E2M1 codes become exact BF16 pairs, the
+//   16 products with x are summed in FP32 (v_dot2_f32_bf16) and the block sum
+//   is multiplied by the block's E4M3 scale into the FP32 accumulator
+//   (x * e2m1 is exact, so this is the product sum x * (e2m1 * e4m3) with a
+//   different FP32 rounding sequence).
+//   BF16 (16 k): plain dot2 products into the accumulator.
+template <bool FP4, int R, int MT>
+__device__ __forceinline__ void tile_compute(const TileRegs<R>& b, const uint16_t* xs,
+                                             int64_t xstride, int64_t t, int M, bool tv,
+                                             float (&acc)[R][MT]) {
+  if (!tv) return;
+  if constexpr (FP4) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      uint32_t xr[MT][8];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          const u32x4* xrow = reinterpret_cast<const u32x4*>(xs + m * xstride);
+          const int64_t q = t * 8 + blk * 2;
+          const u32x4 a = xrow[lds_chunk(q)];
+          const u32x4 c = xrow[lds_chunk(q + 1)];
+          xr[m][0] = a.x; xr[m][1] = a.y; xr[m][2] = a.z; xr[m][3] = a.w;
+          xr[m][4] = c.x; xr[m][5] = c.y; xr[m][6] = c.z; xr[m][7] = c.w;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xr[m][q] = 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t d0 = (blk == 0) ? b.w[i][0].x : (blk == 1) ? b.w[i][0].z : (blk == 2) ? b.w[i][1].x : b.w[i][1].z;
+        const uint32_t d1 = (blk == 0) ? b.w[i][0].y : (blk == 1) ? b.w[i][0].w : (blk == 2) ? b.w[i][1].y : b.w[i][1].w;
+        const uint32_t pr[8] = {e2m1x2_bf16<0>(d0), e2m1x2_bf16<1>(d0), e2m1x2_bf16<2>(d0), e2m1x2_bf16<3>(d0),
+                                e2m1x2_bf16<0>(d1), e2m1x2_bf16<1>(d1), e2m1x2_bf16<2>(d1), e2m1x2_bf16<3>(d1)};
+        float sc;
+        if (blk == 0) sc = e4m3_to_f32<0>(b.s[i]);
+        else if (blk == 1) sc = e4m3_to_f32<1>(b.s[i]);
+        else if (blk == 2) sc = e4m3_to_f32<2>(b.s[i]);
+        else sc = e4m3_to_f32<3>(b.s[i]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float part = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) part = dot2_bf16(pr[q], xr[m][q], part);
+          acc[i][m] = __builtin_fmaf(part, sc, acc[i][m]);
+        }
+      }
+    }
+  } else {
+    uint32_t xr[MT][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        const u32x4* xrow = reinterpret_cast<const u32x4*>(xs + m * xstride);
+        const u32x4 a = xrow[lds_chunk(t * 2)];
+        const u32x4 c = xrow[lds_chunk(t * 2 + 1)];
+        xr[m][0] = a.x; xr[m][1] = a.y; xr[m][2] = a.z; xr[m][3] = a.w;
+        xr[m][4] = c.x; xr[m][5] = c.y; xr[m][6] = c.z; xr[m][7] = c.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xr[m][q] = 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t wd[8] = {b.w[i][0].x, b.w[i][0].y, b.w[i][0].z, b.w[i][0].w,
+                              b.w[i][1].x, b.w[i][1].y, b.w[i][1].z, b.w[i][1].w};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float a = acc[i][m];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a = dot2_bf16(wd[q], xr[m][q], a);
+        acc[i][m] = a;
+      }
+    }
+  }
+}
+
+}  // namespace w4a16
