@@ -42,12 +42,20 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_name(m: int, silu: bool = False) -> str:
-    """Name of the kernel instantiation the library launches for M tokens (NVFP4)."""
-    if m <= 4:
-        mt = 1 if m <= 1 else (2 if m <= 2 else 4)
-        return f"k_gemv_valu<true, {mt}, 64, {str(silu).lower()}>"
-    return f"k_gemv_mfma<true, {1 if m <= 16 else 2}, {str(silu).lower()}>"
+def kernel_name(m: int, k: int, silu: bool = False) -> str:
+    """Kernel instantiation the library launches for an NVFP4 call with M tokens
+    and K columns (mirrors the library's dispatch: the VALU path for M <= 2
+    while M activation rows fit 64 KB, the straight-line form when each lane
+    of a 64-lane group owns one 64-k tile; the MFMA path otherwise)."""
+    sl = str(silu).lower()
+    tiles = k // 64
+    if m <= 2 and m * k * 2 <= 65536:
+        lpq = 64 if tiles > 32 else 32 if tiles > 16 else 16 if tiles > 8 else 8
+        mt = 1 if m <= 1 else 2
+        if tiles <= lpq:
+            return f"k_gemv_valu1<true, {mt}, {lpq}, {sl}>"
+        return f"k_gemv_valu<true, {mt}, {lpq}, {sl}, false>"
+    return f"k_gemv_mfma<true, {1 if m <= 16 else 2}, {sl}>"
 
 
 def source_digest() -> str:
@@ -65,35 +73,39 @@ def algorithmic_bytes(n: int, k: int) -> int:
     return n * k // 2 + synth.flat_scale_bytes(n, k)
 
 
-def cpu_baseline(budget_s: float = 20.0) -> dict:
-    """The binary64 oracle, as it is, on the host cores: sample = the M=1..32
-    sweep on whole 128-row bands of the (4096, 4096) weight, as many bands as
-    fit the time budget (measured on one band first)."""
+def cpu_baseline(budget_s: float = 15.0) -> dict:
+    """The binary64 oracle, as it is, on the host cores, over the same sweep:
+    whole 128-row bands of both weights for every M of the step; the number
+    of bands is sized from a one-band trial so the sample takes about
+    budget_s seconds (a band is a contiguous slice of codes and scales)."""
     import oracle
     import synth
 
     threads = min(len(os.sched_getaffinity(0)), 64)
     oracle.set_threads(threads)
-    n, k = 4096, 4096
-    per_band_bytes = 128 * k // 2 + (k // 64) * 512
-    data = {m: synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m)) for m in SWEEP_M}
+    data = {(n, m): synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, v))
+            for n, k, v in SHAPES for m in SWEEP_M}
 
-    def run(bands: int) -> float:
+    def run(bands: int) -> tuple:
         t0 = time.perf_counter()
-        for m in SWEEP_M:
-            d = data[m]
-            w = d["w"][: 128 * bands].contiguous()
-            s = d["s"][: bands * (k // 64) * 512].contiguous()
-            oracle.nvfp4_gemv(d["x"], w, s, float(d["gs"][0]), 128 * bands)
-        return time.perf_counter() - t0
+        nbytes = 0
+        for n, k, _ in SHAPES:
+            b = min(bands, n // 128)
+            for m in SWEEP_M:
+                d = data[(n, m)]
+                w = d["w"][: 128 * b].contiguous()
+                s = d["s"][: b * (k // 64) * 512].contiguous()
+                oracle.nvfp4_gemv(d["x"], w, s, float(d["gs"][0]), 128 * b)
+                nbytes += 128 * b * k // 2 + b * (k // 64) * 512
+        return time.perf_counter() - t0, nbytes
 
-    t1 = run(1)
-    bands = int(max(1, min(n // 128, budget_s / max(t1, 1e-6))))
-    t = run(bands)
-    gbps = len(SWEEP_M) * bands * per_band_bytes / t / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"M in {SWEEP_M} on {bands} of 32 row bands (128 rows each) of the "
-                      f"N=4096, K=4096 weight ({t:.1f} s, binary64, {threads} threads)"}
+    t1, _ = run(1)
+    bands = int(max(1, min(48, budget_s / max(t1, 1e-6))))
+    t, nbytes = run(bands)
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the M={SWEEP_M} sweep on the first {bands} 128-row bands of the (4096,4096) and "
+                      f"(6144,4096) weights ({nbytes / 1e6:.1f} MB of weight+scale bytes in {t:.1f} s, "
+                      f"binary64, {threads} threads)"}
 
 
 def traffic_record(kernel: str):
@@ -213,7 +225,7 @@ def main() -> int:
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (reps * L)
         nbytes = algorithmic_bytes(c["n"], c["k"])
-        per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": kernel_name(c["m"]),
+        per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": kernel_name(c["m"], c["k"]),
                          "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                          "frac_peak": round(nbytes / us / 1e3 / PEAK_GBPS, 4), "bytes": nbytes})
         log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s")

@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/w4a16_nvfp4_gemv.h"
+#include "w4a16_nvfp4_gemv.h"
 #include "launch.hpp"
 
 namespace {

@@ -55,7 +55,72 @@ __device__ __forceinline__ uint32_t chunks_dummy(int M, uint32_t xstride) {
   return static_cast<uint32_t>(M) * (xstride / 8);
 }
 
+// Single-unit form: every wave-slot owns one unit and every lane exactly one
+// tile (the tiles of a row fit in LPQ lanes), so the whole kernel is straight
+// line code -- activation slice, scale words, the first and then the second
+// 16 bytes of every row are issued back to back, and each half is consumed as
+// soon as it has landed.
 template <bool FP4, int MT, int LPQ, bool SILU>
+__global__ __launch_bounds__(256) void k_gemv_valu1(const GemvParams p) {
+  constexpr int R = SILU ? 8 : 4;
+  constexpr int G = kWave / LPQ;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int li = lane % LPQ;
+  const int slot = lane / LPQ;
+  const int gwave = xcd_logical_block() * 4 + (tid >> 6);
+  const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
+  const int tiles = static_cast<int>(p.tiles);
+  const int unit = gwave * G + slot;
+  const bool tv = unit < static_cast<int>(p.units) && li < tiles;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+
+  // the global scale is read first: left to the epilogue, its load would add
+  // a full memory round trip to the end of every wave
+  const float gs = FP4 ? *p.gs : 1.0f;
+  TileX<FP4, MT> xr;
+  tile_x_global<FP4, MT>(xr, rx, static_cast<uint32_t>(p.ldx) * 2, li, tv, p.M);
+  const UnitRows<R> ur = unit_rows<FP4, SILU, R>(p, unit);
+  TileRegs<R> A;
+  tile_issue<FP4, R>(A, rw, row_bytes, rs, p.tiles, ur.rows, ur.rv, ur.quad_ok, li, tv);
+  // keep every load above ahead of all the arithmetic below
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[R][MT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+  tile_compute_half<FP4, R, MT, 0>(A, xr, acc);
+  tile_compute_half<FP4, R, MT, 1>(A, xr, acc);
+
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = group_sum<LPQ>(acc[i][m]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if ((i * MT + m) % LPQ == li && m < p.M && ur.rv[i]) {
+        if constexpr (!SILU) {
+          p.out[m * static_cast<int64_t>(p.N) + ur.rows[i]] = f32_to_bf16_bits(acc[i][m] * gs);
+        } else {
+          const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][m] * gs));
+          const float up = bf16_bits_to_f32(f32_to_bf16_bits(acc[4 + i][m] * gs));
+          p.out[m * static_cast<int64_t>(p.half) + ur.rows[i]] = f32_to_bf16_bits(silu_f32(g) * up);
+        }
+      }
+    }
+  }
+}
+
+// XREG: every lane owns exactly one tile (K <= 64 * LPQ tiles' worth), so its
+// activation slice is loaded into registers once, before any weight load.
+// Otherwise the workgroup stages all M activation rows in LDS first.
+template <bool FP4, int MT, int LPQ, bool SILU, bool XREG>
 __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
   constexpr int R = SILU ? 8 : 4;
   constexpr int G = kWave / LPQ;  // units a wave works on at once
@@ -71,6 +136,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
   const int gwave = xcd_logical_block() * 4 + (tid >> 6);
   const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
   const uint32_t xstride = (p.K + 63) / 64 * 64;  // LDS row stride (elements)
+  const uint32_t ldx_bytes = static_cast<uint32_t>(p.ldx) * 2;
   const int tiles = static_cast<int>(p.tiles);
   const int units = static_cast<int>(p.units);
   const int ntl = (tiles + LPQ - 1) / LPQ;  // tiles per lane per unit
@@ -81,41 +147,49 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
   const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
 
-  // 1. activations: the first XR chunks of every thread, before any weight load
-  const uint32_t kc = p.K / 8;
-  const uint32_t chunks = static_cast<uint32_t>(p.M) * kc;
+  // 1. activations, before any weight load
+  TileX<FP4, MT> xa, xb;
   u32x4 xv[XR];
   uint32_t xdst[XR];
+  const uint32_t kc = p.K / 8;
+  const uint32_t chunks = static_cast<uint32_t>(p.M) * kc;
+  if constexpr (XREG) {
+    tile_x_global<FP4, MT>(xa, rx, ldx_bytes, li, n_items > 0 && li < tiles, p.M);
+  } else {
 #pragma unroll
-  for (int r = 0; r < XR; ++r) {
-    const uint32_t c = r * 256 + tid;
-    const uint32_t m = c / kc, q = c - m * kc;
-    const bool ok = c < chunks;
-    xv[r] = bload16(rx, ok ? m * static_cast<uint32_t>(p.ldx) * 2 + q * 16 : kOutOfRange);
-    xdst[r] = ok ? m * (xstride / 8) + static_cast<uint32_t>(lds_chunk(q)) : chunks_dummy(p.M, xstride);
+    for (int r = 0; r < XR; ++r) {
+      const uint32_t c = r * 256 + tid;
+      const uint32_t m = c / kc, q = c - m * kc;
+      const bool ok = c < chunks;
+      xv[r] = bload16(rx, ok ? m * ldx_bytes + q * 16 : kOutOfRange);
+      xdst[r] = ok ? m * (xstride / 8) + static_cast<uint32_t>(lds_chunk(q)) : chunks_dummy(p.M, xstride);
+    }
   }
 
-  // 2. first item's weight loads
+  // 2. first item's weight loads (issued unconditionally -- a wave without
+  //    items reads out of range, i.e. nothing -- so that no branch separates
+  //    them from the activation loads)
   TileRegs<R> A, B;
   UnitRows<R> ua, ub;
   bool ta = false, tb = false;
   uint32_t tA = 0, tB = 0;
-  // (issued unconditionally -- a wave without items reads out of range, i.e.
-  // nothing -- so that no branch separates these loads from the x loads)
   ua = unit_rows<FP4, SILU, R>(p, first + slot);
   tA = li;
   ta = n_items > 0 && static_cast<int>(tA) < tiles;
   tile_issue<FP4, R>(A, rw, row_bytes, rs, p.tiles, ua.rows, ua.rv, ua.quad_ok, tA, ta);
 
-  // 3. activations into LDS (swizzled 16-byte chunks; unused slots write a dummy chunk)
-  u32x4* xs4 = reinterpret_cast<u32x4*>(xs);
+  // 3. staged activations into LDS (swizzled 16-byte chunks; unused slots
+  //    write a spare chunk)
+  if constexpr (!XREG) {
+    u32x4* xs4 = reinterpret_cast<u32x4*>(xs);
 #pragma unroll
-  for (int r = 0; r < XR; ++r) xs4[xdst[r]] = xv[r];
-  for (uint32_t c = XR * 256 + tid; c < chunks; c += 256) {
-    const uint32_t m = c / kc, q = c - m * kc;
-    xs4[m * (xstride / 8) + lds_chunk(q)] = bload16(rx, m * static_cast<uint32_t>(p.ldx) * 2 + q * 16);
+    for (int r = 0; r < XR; ++r) xs4[xdst[r]] = xv[r];
+    for (uint32_t c = XR * 256 + tid; c < chunks; c += 256) {
+      const uint32_t m = c / kc, q = c - m * kc;
+      xs4[m * (xstride / 8) + lds_chunk(q)] = bload16(rx, m * ldx_bytes + q * 16);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const float gs = FP4 ? *p.gs : 1.0f;
   float acc[R][MT];
@@ -150,8 +224,8 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
       for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
   };
 
-  // Items run unit batch by unit batch, tile by tile: (ub, tj) is the item
-  // held in buffer B next, advanced without divisions.
+  // Items run unit batch by unit batch, tile by tile: (nb_unit, nb_tj) is the
+  // next item to load, advanced without divisions.
   int nb_unit = first + slot, nb_tj = 0;
   auto advance = [&]() {
     if (++nb_tj == ntl) {
@@ -169,7 +243,8 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
       tile_issue<FP4, R>(B, rw, row_bytes, rs, p.tiles, ub.rows, ub.rv, ub.quad_ok, tB, tb);
       advance();
     }
-    tile_compute<FP4, R, MT>(A, xs, xstride, tA, p.M, ta && ua.rv[0], acc);
+    if constexpr (!XREG) tile_x_lds<FP4, MT>(xa, xs, xstride, tA, p.M);
+    tile_compute<FP4, R, MT>(A, xa, ta && ua.rv[0], acc);
     if ((it % ntl) == ntl - 1) finish_unit(ua);
     if (it + 1 >= n_items) break;
     // B holds item it+1; bring item it+2 into A
@@ -180,7 +255,12 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
       tile_issue<FP4, R>(A, rw, row_bytes, rs, p.tiles, ua.rows, ua.rv, ua.quad_ok, tA, ta);
       advance();
     }
-    tile_compute<FP4, R, MT>(B, xs, xstride, tB, p.M, tb && ub.rv[0], acc);
+    if constexpr (XREG) {
+      tile_compute<FP4, R, MT>(B, xa, tb && ub.rv[0], acc);
+    } else {
+      tile_x_lds<FP4, MT>(xb, xs, xstride, tB, p.M);
+      tile_compute<FP4, R, MT>(B, xb, tb && ub.rv[0], acc);
+    }
     if (((it + 1) % ntl) == ntl - 1) finish_unit(ub);
   }
 }
@@ -193,7 +273,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
 // BF16 tile rows are 16 consecutive rows.
 //
 // One workgroup per row tile (plus the matching up tile with silu_mul); its
-// four waves split K into contiguous quarters and meet in LDS at the end.  A
+// kMfmaWaves waves split K into contiguous slices and meet in LDS at the end.  A
 // step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes feeding 4
 // MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights feeding 1
 // MFMA).  Each wave keeps D steps in flight in a ring: for every step the B
@@ -201,6 +281,8 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
 // in-order wait for a step's x never waits behind the HBM stream, and every
 // ring iteration issues the same loads (steps past the wave's share read
 // zeros through out-of-range offsets), which keeps the waits exact.
+constexpr int kMfmaWaves = 8;
+
 template <bool FP4>
 __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
   if constexpr (FP4) return (tile >> 3) * 128 + (tile & 7) * 4 + (r & 3) + 32 * (r >> 2);
@@ -208,12 +290,13 @@ __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
 }
 
 template <bool FP4, int NT, bool SILU>
-__global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
+__global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams p) {
   constexpr int NA = SILU ? 2 : 1;          // A operands per step (gate, up)
   constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
   constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
-  constexpr int D = FP4 ? (NT == 1 ? 8 : 4) : (NT == 1 ? 16 : 8);  // steps in flight
-  __shared__ f32x4 red[3][NA][NT][64];
+  constexpr int D = FP4 ? 4 : (NT == 1 ? 16 : 8);  // steps in flight per wave
+  constexpr int W = kMfmaWaves;
+  __shared__ f32x4 red[W - 1][NA][NT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -222,7 +305,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
   const int64_t limit = SILU ? p.half : p.N;
   const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
   const int64_t steps_total = (p.K + KSTEP - 1) / KSTEP;
-  const int64_t spw = (steps_total + 3) / 4;           // steps per wave
+  const int64_t spw = (steps_total + W - 1) / W;       // steps per wave
   const int64_t st0 = wave * spw;
   const int64_t nst = st0 < steps_total ? (steps_total - st0 < spw ? steps_total - st0 : spw) : 0;
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
@@ -275,6 +358,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);
+    __builtin_amdgcn_sched_barrier(0);  // all D steps in flight before any arithmetic
 
     f32x4 acc[NA][NT];
 #pragma unroll
@@ -285,43 +369,33 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
     for (int64_t base = 0; base < nst; base += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        u32x4 xc[NJ][NT];
-        u32x4 wc[NA];
-        uint32_t sc[NA];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) xc[j][n] = xb[d][j][n];
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          wc[a] = wb[d][a];
-          sc[a] = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
-        }
-        issue(d, base + d + D);
+        // consume slot d in place, then refill it with step base + d + D
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int a = 0; a < NA; ++a) {
             bf16x8 av;
             if constexpr (FP4) {
-              const float scale = (j < 2) ? e4m3_to_f32<0>(sc[a]) : e4m3_to_f32<1>(sc[a]);
-              const uint32_t word = (j == 0) ? wc[a].x : (j == 1) ? wc[a].y : (j == 2) ? wc[a].z : wc[a].w;
+              const uint32_t sw = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
+              const float scale = (j < 2) ? e4m3_to_f32<0>(sw) : e4m3_to_f32<1>(sw);
+              const uint32_t word = (j == 0) ? wb[d][a].x : (j == 1) ? wb[d][a].y : (j == 2) ? wb[d][a].z : wb[d][a].w;
               uint32_t pr[4];
               dequant_dword(word, scale, pr);
               av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
             } else {
-              av = __builtin_bit_cast(bf16x8, wc[a]);
+              av = __builtin_bit_cast(bf16x8, wb[d][a]);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n)
-              acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xc[j][n]),
+              acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xb[d][j][n]),
                                                                   acc[a][n], 0, 0, 0);
           }
         }
+        issue(d, base + d + D);
       }
     }
 
-    // Four K quarters meet in LDS; wave 0 adds them (quarter order) and writes.
+    // The W K slices meet in LDS; wave 0 adds them in slice order and writes.
     if (wave > 0) {
 #pragma unroll
       for (int a = 0; a < NA; ++a)
@@ -331,10 +405,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const GemvParams p) {
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int w = 0; w < W - 1; ++w)
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          acc[a][n] = ((acc[a][n] + red[0][a][n][lane]) + red[1][a][n][lane]) + red[2][a][n][lane];
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[a][n] += red[w][a][n][lane];
       // C layout: lane holds rows 4(l/16)+i of the tile, token column l%16
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -367,21 +442,31 @@ int lanes_per_unit(int64_t tiles) {
   return 8;
 }
 
-template <bool FP4, int MT, bool SILU>
-hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
-  const int64_t g = kWave / lpq;
+template <bool FP4, int MT, bool SILU, int LPQ>
+hipError_t launch_valu_lpq(const GemvParams& p, hipStream_t stream) {
+  const int64_t g = kWave / LPQ;
   const int64_t waves = (p.units + g - 1) / g;
   int64_t blocks = (waves + 3) / 4;
   if (blocks > 1024) blocks = 1024;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  const size_t lds = static_cast<size_t>(p.M) * ((p.K + 63) / 64 * 64) * 2 + 16;  // + spare chunk
-  switch (lpq) {
-    case 64: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 64, SILU>), grid, block, lds, stream, p); break;
-    case 32: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 32, SILU>), grid, block, lds, stream, p); break;
-    case 16: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 16, SILU>), grid, block, lds, stream, p); break;
-    default: hipLaunchKernelGGL((k_gemv_valu<FP4, MT, 8, SILU>), grid, block, lds, stream, p); break;
+  if (p.tiles <= LPQ) {  // one tile per lane: one unit per wave-slot, straight-line kernel
+    const dim3 grid1(static_cast<unsigned>((waves + 3) / 4));
+    hipLaunchKernelGGL((k_gemv_valu1<FP4, MT, LPQ, SILU>), grid1, block, 0, stream, p);
+  } else {
+    const size_t lds = static_cast<size_t>(p.M) * ((p.K + 63) / 64 * 64) * 2 + 16;  // + spare chunk
+    hipLaunchKernelGGL((k_gemv_valu<FP4, MT, LPQ, SILU, false>), grid, block, lds, stream, p);
   }
   return hipGetLastError();
+}
+
+template <bool FP4, int MT, bool SILU>
+hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
+  switch (lpq) {
+    case 64: return launch_valu_lpq<FP4, MT, SILU, 64>(p, stream);
+    case 32: return launch_valu_lpq<FP4, MT, SILU, 32>(p, stream);
+    case 16: return launch_valu_lpq<FP4, MT, SILU, 16>(p, stream);
+    default: return launch_valu_lpq<FP4, MT, SILU, 8>(p, stream);
+  }
 }
 
 template <bool FP4, int NT, bool SILU>
@@ -390,8 +475,8 @@ hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   p.units = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   int64_t blocks = p.units;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kMfmaWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -403,8 +488,7 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
     p.units = FP4 ? ((limit + 127) / 128) * 32 : (limit + 3) / 4;
     const int lpq = lanes_per_unit(p.tiles);
     if (p.M <= 1) return launch_valu<FP4, 1, SILU>(p, lpq, stream);
-    if (p.M <= 2) return launch_valu<FP4, 2, SILU>(p, lpq, stream);
-    return launch_valu<FP4, 4, SILU>(p, lpq, stream);
+    return launch_valu<FP4, 2, SILU>(p, lpq, stream);
   }
   p.tiles = p.K / 64;
   if (p.M <= 16) return launch_mfma<FP4, 1, SILU>(p, stream);
@@ -419,7 +503,7 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
 // forces a path (the tests use it to cover both at every M).
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K) {
   (void)N;
-  const bool valu_fits = M <= 4 && M * ((K + 63) / 64 * 64) * 2 <= 65536;
+  const bool valu_fits = M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536;
   if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
     if (std::strcmp(env, "mfma") == 0) return kPathMfma;
     if (std::strcmp(env, "valu") == 0 && valu_fits) return kPathValu;

@@ -228,12 +228,16 @@ __device__ __forceinline__ void tile_issue(TileRegs<R>& b, rsrc_t w, uint32_t ro
       }
     }
   }
+  uint32_t off[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const uint32_t off = (tv && rv[i]) ? static_cast<uint32_t>(rows[i]) * row_bytes + t * 32 : kOutOfRange;
-    b.w[i][0] = bload16_nt(w, off);
-    b.w[i][1] = bload16_nt(w, off + 16);
-  }
+  for (int i = 0; i < R; ++i)
+    off[i] = (tv && rv[i]) ? static_cast<uint32_t>(rows[i]) * row_bytes + t * 32 : kOutOfRange;
+  // first 16 bytes of every row, then the second 16: the first half of the
+  // tile can be consumed while the second is still arriving
+#pragma unroll
+  for (int i = 0; i < R; ++i) b.w[i][0] = bload16_nt(w, off[i]);
+#pragma unroll
+  for (int i = 0; i < R; ++i) b.w[i][1] = bload16_nt(w, off[i] + 16);
 }
 
 // Position of 16-byte chunk q of a staged activation row in LDS.  Lanes read
@@ -246,85 +250,116 @@ __device__ __forceinline__ uint32_t e2m1x2_bf16(uint32_t word) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL));
 }
 
-// Accumulates one staged tile.  x comes from LDS: xs points at token 0 of the
-// staged activations, xstride elements per token.
-//   NVFP4 (64 k): per 16-k block, the E2M1 codes become exact BF16 pairs, the
-//   16 products with x are summed in FP32 (v_dot2_f32_bf16) and the block sum
-//   is multiplied by the block's E4M3 scale into the FP32 accumulator
-//   (x * e2m1 is exact, so this is the product sum x * (e2m1 * e4m3) with a
-//   different FP32 rounding sequence).
-//   BF16 (16 k): plain dot2 products into the accumulator.
-template <bool FP4, int R, int MT>
-__device__ __forceinline__ void tile_compute(const TileRegs<R>& b, const uint16_t* xs,
-                                             int64_t xstride, int64_t t, int M, bool tv,
-                                             float (&acc)[R][MT]) {
-  if (!tv) return;
+// Activation slice of one tile for MT tokens: NVFP4 tiles are 64 k (32 bf16
+// pairs per token), BF16 tiles 16 k (8 pairs).
+template <bool FP4, int MT>
+struct TileX {
+  uint32_t v[MT][FP4 ? 32 : 8];
+};
+
+// The slice of tile t from the LDS staging area (xs: token 0, xstride
+// elements per token, 16-byte chunks placed by lds_chunk).
+template <bool FP4, int MT>
+__device__ __forceinline__ void tile_x_lds(TileX<FP4, MT>& x, const uint16_t* xs, uint32_t xstride,
+                                           uint32_t t, int M) {
+  constexpr int C = FP4 ? 8 : 2;  // 16-byte chunks per tile
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(xs + (m < M ? m : 0) * xstride);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const u32x4 v = xrow[lds_chunk(t * C + c)];
+      x.v[m][4 * c + 0] = m < M ? v.x : 0u;
+      x.v[m][4 * c + 1] = m < M ? v.y : 0u;
+      x.v[m][4 * c + 2] = m < M ? v.z : 0u;
+      x.v[m][4 * c + 3] = m < M ? v.w : 0u;
+    }
+  }
+}
+
+// The slice of tile t straight from global memory (buffer loads; tokens past
+// M and tiles past K read zero).
+template <bool FP4, int MT>
+__device__ __forceinline__ void tile_x_global(TileX<FP4, MT>& x, rsrc_t rx, uint32_t ldx_bytes,
+                                              uint32_t t, bool tv, int M) {
+  constexpr int C = FP4 ? 8 : 2;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const uint32_t off = (tv && m < M) ? m * ldx_bytes + (t * C + c) * 16 : kOutOfRange;
+      const u32x4 v = bload16(rx, off);
+      x.v[m][4 * c + 0] = v.x;
+      x.v[m][4 * c + 1] = v.y;
+      x.v[m][4 * c + 2] = v.z;
+      x.v[m][4 * c + 3] = v.w;
+    }
+  }
+}
+
+// Accumulates half H (0: k 0..31, 1: k 32..63 of an NVFP4 tile; 0: k 0..7,
+// 1: k 8..15 of a BF16 tile) of one tile; rows are interleaved so that the
+// per-row dot chains are independent.
+//   NVFP4: per 16-k block, the E2M1 codes become exact BF16 pairs, the 16
+//   products with x are summed in FP32 (v_dot2_f32_bf16) and the block sum is
+//   multiplied by the block's E4M3 scale into the FP32 accumulator (x * e2m1
+//   is exact, so this is the product sum x * (e2m1 * e4m3) with a different
+//   FP32 rounding sequence).
+//   BF16: plain dot2 products into the accumulator.
+template <bool FP4, int R, int MT, int H>
+__device__ __forceinline__ void tile_compute_half(const TileRegs<R>& b, const TileX<FP4, MT>& x,
+                                                  float (&acc)[R][MT]) {
   if constexpr (FP4) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      uint32_t xr[MT][8];
+    for (int bb = 0; bb < 2; ++bb) {
+      const int blk = 2 * H + bb;
+      float part[R][MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const u32x4* xrow = reinterpret_cast<const u32x4*>(xs + m * xstride);
-          const int64_t q = t * 8 + blk * 2;
-          const u32x4 a = xrow[lds_chunk(q)];
-          const u32x4 c = xrow[lds_chunk(q + 1)];
-          xr[m][0] = a.x; xr[m][1] = a.y; xr[m][2] = a.z; xr[m][3] = a.w;
-          xr[m][4] = c.x; xr[m][5] = c.y; xr[m][6] = c.z; xr[m][7] = c.w;
-        } else {
+      for (int i = 0; i < R; ++i) {
+        const uint32_t d0 = bb == 0 ? b.w[i][H].x : b.w[i][H].z;
+        const uint32_t d1 = bb == 0 ? b.w[i][H].y : b.w[i][H].w;
+        const uint32_t pr[8] = {e2m1x2_bf16<0>(d0), e2m1x2_bf16<1>(d0), e2m1x2_bf16<2>(d0), e2m1x2_bf16<3>(d0),
+                                e2m1x2_bf16<0>(d1), e2m1x2_bf16<1>(d1), e2m1x2_bf16<2>(d1), e2m1x2_bf16<3>(d1)};
 #pragma unroll
-          for (int q = 0; q < 8; ++q) xr[m][q] = 0;
+        for (int m = 0; m < MT; ++m) {
+          float a = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) a = dot2_bf16(pr[q], x.v[m][8 * blk + q], a);
+          part[i][m] = a;
         }
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const uint32_t d0 = (blk == 0) ? b.w[i][0].x : (blk == 1) ? b.w[i][0].z : (blk == 2) ? b.w[i][1].x : b.w[i][1].z;
-        const uint32_t d1 = (blk == 0) ? b.w[i][0].y : (blk == 1) ? b.w[i][0].w : (blk == 2) ? b.w[i][1].y : b.w[i][1].w;
-        const uint32_t pr[8] = {e2m1x2_bf16<0>(d0), e2m1x2_bf16<1>(d0), e2m1x2_bf16<2>(d0), e2m1x2_bf16<3>(d0),
-                                e2m1x2_bf16<0>(d1), e2m1x2_bf16<1>(d1), e2m1x2_bf16<2>(d1), e2m1x2_bf16<3>(d1)};
         float sc;
         if (blk == 0) sc = e4m3_to_f32<0>(b.s[i]);
         else if (blk == 1) sc = e4m3_to_f32<1>(b.s[i]);
         else if (blk == 2) sc = e4m3_to_f32<2>(b.s[i]);
         else sc = e4m3_to_f32<3>(b.s[i]);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          float part = 0.0f;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) part = dot2_bf16(pr[q], xr[m][q], part);
-          acc[i][m] = __builtin_fmaf(part, sc, acc[i][m]);
-        }
+        for (int m = 0; m < MT; ++m) acc[i][m] = __builtin_fmaf(part[i][m], sc, acc[i][m]);
       }
     }
   } else {
-    uint32_t xr[MT][8];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < M) {
-        const u32x4* xrow = reinterpret_cast<const u32x4*>(xs + m * xstride);
-        const u32x4 a = xrow[lds_chunk(t * 2)];
-        const u32x4 c = xrow[lds_chunk(t * 2 + 1)];
-        xr[m][0] = a.x; xr[m][1] = a.y; xr[m][2] = a.z; xr[m][3] = a.w;
-        xr[m][4] = c.x; xr[m][5] = c.y; xr[m][6] = c.z; xr[m][7] = c.w;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xr[m][q] = 0;
-      }
-    }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const uint32_t wd[8] = {b.w[i][0].x, b.w[i][0].y, b.w[i][0].z, b.w[i][0].w,
-                              b.w[i][1].x, b.w[i][1].y, b.w[i][1].z, b.w[i][1].w};
+      const uint32_t wd[4] = {b.w[i][H].x, b.w[i][H].y, b.w[i][H].z, b.w[i][H].w};
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         float a = acc[i][m];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a = dot2_bf16(wd[q], xr[m][q], a);
+        for (int q = 0; q < 4; ++q) a = dot2_bf16(wd[q], x.v[m][4 * H + q], a);
         acc[i][m] = a;
       }
     }
   }
+}
+
+template <bool FP4, int R, int MT>
+__device__ __forceinline__ void tile_compute(const TileRegs<R>& b, const TileX<FP4, MT>& x, bool tv,
+                                             float (&acc)[R][MT]) {
+  if (!tv) return;
+  tile_compute_half<FP4, R, MT, 0>(b, x, acc);
+  tile_compute_half<FP4, R, MT, 1>(b, x, acc);
 }
 
 }  // namespace w4a16
