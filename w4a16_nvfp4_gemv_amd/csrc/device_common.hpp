@@ -151,6 +151,57 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Reduce-scatter of V per-lane values over the 64 lanes of a wave, down to P
+// values per lane (P = 1, or 2 to keep pairs such as gate/up together).
+// v_permlane32_swap exchanges the upper half-wave of its first operand with the
+// lower half-wave of its second, so one swap and one add sum value j over lanes
+// {l, l^32} in the lower half-wave and value j + V/2 in the upper one;
+// v_permlane16_swap does the same between odd and even 16-lane rows.  The
+// values left are then summed over the remaining 16/32/64 lanes with
+// group_sum.  On return lane l holds, in v[0..P'-1], the full sums of values
+// base + 0..P'-1, base = reduce_scatter_base<V, P>(l).
+template <int V, int P>
+struct ReduceScatter {
+  static constexpr bool S32 = V >= 2 * P;
+  static constexpr bool S16 = V >= 4 * P;
+  static constexpr int LEFT = S16 ? V / 4 : (S32 ? V / 2 : V);  // values per lane at the end
+  static constexpr int SPAN = S16 ? 16 : (S32 ? 32 : 64);       // lanes still to sum over
+};
+
+template <int V, int P>
+__device__ __forceinline__ int reduce_scatter_base(int lane) {
+  using RS = ReduceScatter<V, P>;
+  int base = 0;
+  if constexpr (RS::S32) base += (lane >> 5) * (V / 2);
+  if constexpr (RS::S16) base += ((lane >> 4) & 1) * (V / 4);
+  return base;
+}
+
+template <int V, int P>
+__device__ __forceinline__ void reduce_scatter(float (&v)[V]) {
+  using RS = ReduceScatter<V, P>;
+  if constexpr (RS::S32) {
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                      __builtin_bit_cast(uint32_t, v[j + V / 2]), false, false);
+      v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) +
+             __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+    }
+  }
+  if constexpr (RS::S16) {
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                      __builtin_bit_cast(uint32_t, v[j + V / 4]), false, false);
+      v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) +
+             __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RS::LEFT; ++j) v[j] = group_sum<RS::SPAN>(v[j]);
+}
+
 // ---------------------------------------------------------------- XCD order
 // Workgroups are dispatched round-robin over the 8 XCDs (hardware id b runs on
 // XCD b % 8).  Renumbering them so that consecutive logical ids share an XCD

@@ -265,6 +265,155 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
   }
 }
 
+// ------------------------------------------------------------------ VALU, chunked
+// NVFP4 form of the VALU path in which every load instruction of a wave reads
+// one contiguous stretch of memory.  A unit is one quad (plus its up quad with
+// silu_mul) and KS waves of a workgroup share it, each taking a contiguous
+// slice of K.  K is cut into 8-k chunks -- 4 code bytes of a row, 16
+// activation bytes of a token -- and lane l of slice s owns chunks
+// (s*C + c)*64 + l for c < C, so a chunk load of the wave covers 256
+// contiguous bytes of a weight row or 1 KB of an activation row.  The scale of
+// chunk ch is byte (ch/2) % 4 = (l/2) % 4 of its row's word in tile ch/8: the
+// lane reads the quad's 16-byte scale chunk of that tile and shifts by a fixed
+// amount.  All loads are issued up front (activations, scales, then weights
+// chunk by chunk), the 8 products of a chunk are summed in FP32 and scaled
+// once, each wave's partial sums meet through a permlane reduce-scatter, and
+// the KS slices are added in slice order through LDS.
+template <int MT, bool SILU, int C, int KS>
+__global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
+  constexpr int R = SILU ? 8 : 4;
+  constexpr int NQ = R / 4;
+  constexpr int P = SILU ? 2 : 1;
+  constexpr int V = MT * 4 * P;  // value index v = (m * 4 + q) * P + u
+  using RS = ReduceScatter<V, P>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kw = wave % KS;
+  const int unit = xcd_logical_block() * (4 / KS) + wave / KS;
+  const uint32_t row_bytes = p.K / 2;
+  const uint32_t nch = p.K / 8;
+  const uint32_t ch0 = static_cast<uint32_t>(kw * C) * 64 + lane;
+  const uint32_t ldx_bytes = static_cast<uint32_t>(p.ldx) * 2;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+
+  const float gs = *p.gs;
+  const UnitRows<R> ur = unit_rows<true, SILU, R>(p, unit);
+
+  u32x4 xv[MT][C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ch = ch0 + c * 64;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      xv[m][c] = bload16(rx, (ch < nch && m < p.M) ? m * ldx_bytes + ch * 16 : kOutOfRange);
+  }
+  uint32_t sw[C][R];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ch = ch0 + c * 64;
+    const uint32_t t = ch >> 3;
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      if (ur.quad_ok[h]) {
+        const bool ok = ch < nch && ur.rv[4 * h];
+        const u32x4 sc = bload16(rs, ok ? static_cast<uint32_t>(scale_word_offset(ur.rows[4 * h], t, p.tiles))
+                                        : kOutOfRange);
+        sw[c][4 * h + 0] = sc.x;
+        sw[c][4 * h + 1] = sc.y;
+        sw[c][4 * h + 2] = sc.z;
+        sw[c][4 * h + 3] = sc.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = ch < nch && ur.rv[4 * h + j];
+          sw[c][4 * h + j] =
+              bload4(rs, ok ? static_cast<uint32_t>(scale_word_offset(ur.rows[4 * h + j], t, p.tiles)) : kOutOfRange);
+        }
+      }
+    }
+  }
+  uint32_t wv[C][R];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ch = ch0 + c * 64;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      wv[c][i] = bload4(rw, (ch < nch && ur.rv[i]) ? static_cast<uint32_t>(ur.rows[i]) * row_bytes + ch * 4
+                                                    : kOutOfRange);
+  }
+  // every load above stays ahead of the arithmetic below
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t shift = 8u * ((lane >> 1) & 3);
+  float acc[R][MT];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t pr[4] = {e2m1x2_bf16<0>(wv[c][i]), e2m1x2_bf16<1>(wv[c][i]), e2m1x2_bf16<2>(wv[c][i]),
+                              e2m1x2_bf16<3>(wv[c][i])};
+      const float sc = e4m3_to_f32<0>(sw[c][i] >> shift);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float a = dot2_bf16(pr[0], xv[m][c].x, 0.0f);
+        a = dot2_bf16(pr[1], xv[m][c].y, a);
+        a = dot2_bf16(pr[2], xv[m][c].z, a);
+        a = dot2_bf16(pr[3], xv[m][c].w, a);
+        acc[i][m] = __builtin_fmaf(a, sc, acc[i][m]);
+      }
+    }
+  }
+
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < P; ++u) v[(m * 4 + q) * P + u] = acc[4 * u + q][m];
+  reduce_scatter<V, P>(v);
+  if constexpr (KS > 1) {
+    __shared__ float red[4][RS::LEFT][64];
+    if (kw > 0) {
+#pragma unroll
+      for (int j = 0; j < RS::LEFT; ++j) red[wave][j][lane] = v[j];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int s2 = 1; s2 < KS; ++s2)
+#pragma unroll
+        for (int j = 0; j < RS::LEFT; ++j) v[j] += red[wave + s2][j][lane];
+    }
+  }
+  const int base = reduce_scatter_base<V, P>(lane);
+  // the row is computed, not looked up: a lane-dependent index into ur.rows
+  // would move the array to LDS
+  const int64_t limit = SILU ? p.half : p.N;
+#pragma unroll
+  for (int j = 0; j < RS::LEFT / P; ++j) {
+    const int vi = base + j * P;
+    const int m = vi / (4 * P), q = (vi / P) % 4;
+    const int64_t row = (static_cast<int64_t>(unit) >> 5) * 128 + (unit & 31) + 32 * q;
+    if (kw == 0 && (lane & 15) == j && m < p.M && unit < p.units && row < limit) {
+      if constexpr (!SILU) {
+        p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[j] * gs);
+      } else {
+        const float g = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P] * gs));
+        const float up = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P + 1] * gs));
+        p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(g) * up);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ MFMA
 // Swap-AB MFMA path.  A row tile is 16 weight rows, the A operand of
 // v_mfma_f32_16x16x32_bf16; the B operand holds up to 16 tokens (two token
@@ -459,6 +608,51 @@ hipError_t launch_valu_lpq(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MT, bool SILU, int C, int KS>
+hipError_t launch_vchunk_c(const GemvParams& p, hipStream_t stream) {
+  constexpr int upb = 4 / KS;
+  const dim3 grid(static_cast<unsigned>((p.units + upb - 1) / upb)), block(256);
+  hipLaunchKernelGGL((k_gemv_vchunk<MT, SILU, C, KS>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+// Largest M the NVFP4 GEMV sends to the VALU path by default.
+constexpr int64_t kValuMaxMFp4 = 4;
+
+// NVFP4 rows of at most kVchunkMaxK columns: 8-k chunks, at most 8 per lane
+// and 4 waves per unit.
+constexpr int64_t kVchunkMaxK = 64 * 8 * 8 * 4;
+
+template <int MT, bool SILU, int KS>
+hipError_t launch_vchunk_ks(const GemvParams& p, hipStream_t stream) {
+  const int64_t per_lane = (p.K / 8 + 64 * KS - 1) / (64 * KS);
+  if (per_lane <= 1) return launch_vchunk_c<MT, SILU, 1, KS>(p, stream);
+  if (per_lane <= 2) return launch_vchunk_c<MT, SILU, 2, KS>(p, stream);
+  if (per_lane <= 4) return launch_vchunk_c<MT, SILU, 4, KS>(p, stream);
+  return launch_vchunk_c<MT, SILU, 8, KS>(p, stream);
+}
+
+// Waves per unit: four for one or two tokens, two for four tokens (whose
+// activation registers would otherwise crowd out the loads in flight), fewer
+// when K has too few 8-k chunks to give every lane of every wave one, more
+// when a lane would need more than 8 chunks.
+int vchunk_ks(int MT, int64_t K) {
+  const int64_t chunks = K / 8;
+  int ks = MT <= 2 ? 4 : 2;
+  while (ks > 1 && 64 * ks > chunks) ks /= 2;
+  while (ks < 4 && chunks > 512 * ks) ks *= 2;
+  return ks;
+}
+
+template <int MT, bool SILU>
+hipError_t launch_vchunk(const GemvParams& p, hipStream_t stream) {
+  switch (vchunk_ks(MT, p.K)) {
+    case 1: return launch_vchunk_ks<MT, SILU, 1>(p, stream);
+    case 2: return launch_vchunk_ks<MT, SILU, 2>(p, stream);
+    default: return launch_vchunk_ks<MT, SILU, 4>(p, stream);
+  }
+}
+
 template <bool FP4, int MT, bool SILU>
 hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
   switch (lpq) {
@@ -486,6 +680,13 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   if (path == kPathValu) {
     p.tiles = FP4 ? p.K / 64 : p.K / 16;
     p.units = FP4 ? ((limit + 127) / 128) * 32 : (limit + 3) / 4;
+    if constexpr (FP4) {
+      if (p.K <= kVchunkMaxK) {
+        if (p.M <= 1) return launch_vchunk<1, SILU>(p, stream);
+        if (p.M <= 2) return launch_vchunk<2, SILU>(p, stream);
+        return launch_vchunk<4, SILU>(p, stream);
+      }
+    }
     const int lpq = lanes_per_unit(p.tiles);
     if (p.M <= 1) return launch_valu<FP4, 1, SILU>(p, lpq, stream);
     return launch_valu<FP4, 2, SILU>(p, lpq, stream);
@@ -497,18 +698,20 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
 
 }  // namespace
 
-// VALU dot path while the activations fit the 64 KB staging area and the
-// per-weight VALU work (about 0.5 + 0.5 M instructions) stays below the MFMA
-// path's dequantization cost; MFMA otherwise.  W4A16_GEMV_PATH=valu|mfma
-// forces a path (the tests use it to cover both at every M).
+// VALU dot path for the smallest M and the MFMA path above it.  NVFP4 rows
+// of up to kVchunkMaxK columns take the chunked VALU kernel (M <= 4); other
+// VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
+// W4A16_GEMV_PATH=valu|mfma forces a path where it applies (the tests use it
+// to cover both at every M).
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K) {
   (void)N;
-  const bool valu_fits = M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536;
+  const bool chunked = fp4 && K <= kVchunkMaxK;
+  const bool valu_fits = chunked ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
   if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
     if (std::strcmp(env, "mfma") == 0) return kPathMfma;
     if (std::strcmp(env, "valu") == 0 && valu_fits) return kPathValu;
   }
-  const int64_t valu_max_m = fp4 ? 2 : 1;
+  const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : 1;
   return (valu_fits && M <= valu_max_m) ? kPathValu : kPathMfma;
 }
 
