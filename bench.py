@@ -6,22 +6,36 @@ One step is one pass of the dense W4A16 GEMV sweep: M in {1,2,4,8,16,32} on
 the (N, K) = (4096, 4096) and (6144, 4096) weights, 12 nvfp4_gemv calls.
 Every call reads its own copy of the weight and scales: 60 copies of each
 weight rotate (566 MB and 849 MB, each more than the 256 MB Infinity Cache),
-so weights come from HBM.  The
-12 launches of a step are captured once into a HIP graph per copy set and
-replayed, so the host's launch overhead does not throttle the GPU.
+so weights come from HBM.  The 12 launches of a step are captured once into
+a HIP graph per copy set and replayed, so the host's launch overhead does
+not throttle the GPU.
 
 value = algorithmic bytes of a step (packed weight + flat scale bytes of the
 12 calls) / wall time per step, in GB/s.  Activation and output bytes are not
 counted.  Each per-call figure comes from HIP events around a graph of 64
-back-to-back launches of that one call shape.  The roofline object reports the
-kernel with the largest share of the step.  The CPU baseline is the binary64
-oracle on the host cores over a bounded sample of the same workload.
+back-to-back launches of that one call shape on the stream the graph runs
+on.  The roofline object reports the kernel with the largest share of the
+step, with its HBM traffic from the committed rocprofv3 counter runs when
+they were taken on the current kernel sources.  The CPU baseline is the
+binary64 oracle on the host cores over whole steps of the same workload.
+The "extras" list times the other workloads of the family (fused gate|up
+SiLU GEMV, BF16-weight GEMV, MoE decode pair) the same way; they are not
+part of the step.
+
+Two helper modes feed profiles/traffic_counters.json:
+    rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --counter-pass
+    rocprofv3 --pmc WRITE_SIZE ... -- python3 bench.py --counter-pass
+    python bench.py --ingest-counters FETCH_CSV WRITE_CSV
+The counter pass launches every call of the step four times, eagerly, then
+copies a 64 MiB buffer three times; the copy of known size calibrates each
+counter.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -36,32 +50,24 @@ PEAK_GBPS = 8000.0
 SWEEP_M = [1, 2, 4, 8, 16, 32]
 SHAPES = [(4096, 4096, 0), (6144, 4096, 1)]
 COPY_SETS = 10  # step graphs; each reads 6 fresh copies of each weight
+COUNTER_LAUNCHES = 4
+CALIB_BYTES = 64 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_name(m: int, k: int, silu: bool = False) -> str:
-    """Kernel instantiation the library launches for an NVFP4 call with M tokens
-    and K columns (mirrors the library's dispatch: the VALU path for M <= 2
-    while M activation rows fit 64 KB, the straight-line form when each lane
-    of a 64-lane group owns one 64-k tile; the MFMA path otherwise)."""
-    sl = str(silu).lower()
-    tiles = k // 64
-    if m <= 2 and m * k * 2 <= 65536:
-        lpq = 64 if tiles > 32 else 32 if tiles > 16 else 16 if tiles > 8 else 8
-        mt = 1 if m <= 1 else 2
-        if tiles <= lpq:
-            return f"k_gemv_valu1<true, {mt}, {lpq}, {sl}>"
-        return f"k_gemv_valu<true, {mt}, {lpq}, {sl}, false>"
-    return f"k_gemv_mfma<true, {1 if m <= 16 else 2}, {sl}>"
+# the sources the dense GEMV kernels are compiled from
+GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "unit_core.hpp", "launch.hpp"]
 
 
 def source_digest() -> str:
+    """Digest of the dense GEMV kernel sources: counter figures taken on other sources are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_nvfp4_gemv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMV_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -73,48 +79,52 @@ def algorithmic_bytes(n: int, k: int) -> int:
     return n * k // 2 + synth.flat_scale_bytes(n, k)
 
 
-def cpu_baseline(budget_s: float = 15.0) -> dict:
-    """The binary64 oracle, as it is, on the host cores, over the same sweep:
-    whole 128-row bands of both weights for every M of the step; the number
-    of bands is sized from a one-band trial so the sample takes about
-    budget_s seconds (a band is a contiguous slice of codes and scales)."""
+def cpu_threads() -> int:
+    avail = len(os.sched_getaffinity(0))
+    try:
+        want = int(os.environ.get("OMP_NUM_THREADS", avail))
+    except ValueError:
+        want = avail
+    return max(1, min(avail, want))
+
+
+def cpu_baseline(budget_s: float) -> dict:
+    """The binary64 oracle, as it is, on the host cores: whole steps of the
+    sweep (all 12 calls at full size) repeated to fill about budget_s seconds
+    (the repeat count is sized from one untimed-for-the-figure step)."""
     import oracle
     import synth
 
-    threads = min(len(os.sched_getaffinity(0)), 64)
+    threads = cpu_threads()
     oracle.set_threads(threads)
-    data = {(n, m): synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, v))
-            for n, k, v in SHAPES for m in SWEEP_M}
+    data = [(n, synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, v)))
+            for n, k, v in SHAPES for m in SWEEP_M]
+    step_bytes = sum(algorithmic_bytes(n, k) for n, k, _ in SHAPES) * len(SWEEP_M)
 
-    def run(bands: int) -> tuple:
-        t0 = time.perf_counter()
-        nbytes = 0
-        for n, k, _ in SHAPES:
-            b = min(bands, n // 128)
-            for m in SWEEP_M:
-                d = data[(n, m)]
-                w = d["w"][: 128 * b].contiguous()
-                s = d["s"][: b * (k // 64) * 512].contiguous()
-                oracle.nvfp4_gemv(d["x"], w, s, float(d["gs"][0]), 128 * b)
-                nbytes += 128 * b * k // 2 + b * (k // 64) * 512
-        return time.perf_counter() - t0, nbytes
+    def step():
+        for n, d in data:
+            oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
 
-    t1, _ = run(1)
-    bands = int(max(1, min(48, budget_s / max(t1, 1e-6))))
-    t, nbytes = run(bands)
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the M={SWEEP_M} sweep on the first {bands} 128-row bands of the (4096,4096) and "
-                      f"(6144,4096) weights ({nbytes / 1e6:.1f} MB of weight+scale bytes in {t:.1f} s, "
-                      f"binary64, {threads} threads)"}
+    t0 = time.perf_counter()
+    step()
+    t1 = time.perf_counter() - t0
+    reps = max(1, int(round(budget_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    t = time.perf_counter() - t0
+    return {"value": round(step_bytes * reps / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full 12-call step (M={SWEEP_M} on the (4096,4096) and (6144,4096) weights, "
+                      f"{step_bytes / 1e6:.1f} MB of weight+scale bytes) repeated {reps} times in {t:.1f} s, "
+                      f"binary64, {threads} OpenMP threads"}
 
 
 def traffic_record(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when they are missing or were taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs, or None when they are missing or were taken on other sources."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
     if rec.get("source_digest") != source_digest():
         return None
@@ -122,45 +132,101 @@ def traffic_record(kernel: str):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+# ---------------------------------------------------------------- counters
+def _short_kernel(name: str) -> str:
+    """'void w4a16::k_gemv_mfma<true, 1, false>(w4a16::GemvParams)' -> 'k_gemv_mfma<true, 1, false>'."""
+    s = name.strip().strip('"')
+    if s.startswith("void "):
+        s = s[5:]
+    if "(" in s:
+        s = s[: s.index("(")]
+    return s.split("::")[-1] if s.startswith("w4a16::") else s
+
+
+def ingest_counters(fetch_csv: str, write_csv: str) -> int:
+    """Per-kernel HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE
+    counter_collection.csv of the counter pass, each counter scaled by what it
+    reads for the 64 MiB copy of the same run; writes TRAFFIC_FILE."""
+    def per_kernel(path: str, counter: str):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-3:]
+        if len(copies) < 3:
+            raise SystemExit(f"{path}: the three calibration copies are missing")
+        kib_per_copy = sum(copies) / len(copies)
+        # the copy reads CALIB_BYTES and writes CALIB_BYTES
+        scale = (CALIB_BYTES / 1024.0) / kib_per_copy
+        out = {}
+        for r in rows:
+            k = _short_kernel(r["Kernel_Name"])
+            if not k.startswith("k_"):
+                continue
+            out.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}, kib_per_copy, scale
+
+    fetch, fetch_copy, fscale = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, write_copy, wscale = per_kernel(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        fb = fetch.get(k, 0.0) * fscale * 1024
+        wb = write.get(k, 0.0) * wscale * 1024
+        kernels[k] = {"fetch_kib_raw": round(fetch.get(k, 0.0), 3), "write_kib_raw": round(write.get(k, 0.0), 3),
+                      "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    rec = {"source_digest": source_digest(),
+           "calibration": {"copy_bytes": CALIB_BYTES,
+                           "fetch_kib_per_copy": round(fetch_copy, 3), "fetch_scale": round(fscale, 5),
+                           "write_kib_per_copy": round(write_copy, 3), "write_scale": round(wscale, 5)},
+           "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
+# ---------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--per-call-launches", type=int, default=64)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               "requested).  Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.ingest_counters:
+        return ingest_counters(*args.ingest_counters)
 
     import torch
 
     import synth
-    from w4a16_nvfp4_gemv_amd import _lib
+    from w4a16_nvfp4_gemv_amd import _lib, gemv_kernel_name
 
     lib = _lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    n_copies = COUNTER_LAUNCHES if args.counter_pass else COPY_SETS * len(SWEEP_M)
 
     # ---------------------------------------------------------------- inputs
-    calls = []  # (n, k, m, x, w_copies, s_copies, gs, out)
+    calls = []
     for n, k, variant in SHAPES:
         base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(1, 1, variant))
         w0 = base["w"].to(dev)
         s0 = base["s"].to(dev)
-        copies_w = [w0] + [w0.clone() for _ in range(COPY_SETS * len(SWEEP_M) - 1)]
-        copies_s = [s0] + [s0.clone() for _ in range(COPY_SETS * len(SWEEP_M) - 1)]
+        copies_w = [w0] + [w0.clone() for _ in range(n_copies - 1)]
+        copies_s = [s0] + [s0.clone() for _ in range(n_copies - 1)]
         for j, m in enumerate(SWEEP_M):
             d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, variant))
-            x = d["x"].to(dev)
-            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            calls.append(dict(n=n, k=k, m=m, j=j, x=x, gs=d["gs"].to(dev), out=out,
-                              w=copies_w, s=copies_s))
-    resident = sum(c["w"][0].numel() + c["s"][0].numel() for c in calls[::len(SWEEP_M)]) * COPY_SETS * len(SWEEP_M)
-    log(f"weight copies resident: {resident / 1e6:.0f} MB")
+            calls.append(dict(n=n, k=k, m=m, j=j, x=d["x"].to(dev), gs=d["gs"].to(dev),
+                              out=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+                              w=copies_w, s=copies_s, kernel=gemv_kernel_name(m, n, k)))
 
     def launch(c, copy_idx, stream):
         st = lib.nvfp4_gemv(c["x"].data_ptr(), c["m"], c["k"], c["x"].stride(0),
@@ -169,13 +235,29 @@ def main() -> int:
         if st != 0:
             raise RuntimeError(f"nvfp4_gemv failed: {lib.w4a16_last_error().decode()}")
 
+    if args.counter_pass:
+        stream = torch.cuda.current_stream().cuda_stream
+        for c in calls:
+            for i in range(COUNTER_LAUNCHES):
+                launch(c, i, stream)
+        torch.cuda.synchronize()
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        src.fill_(3)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("counter pass done:", ", ".join(sorted({c["kernel"] for c in calls})))
+        return 0
+
+    resident = sum(c["w"][0].numel() + c["s"][0].numel() for c in calls[::len(SWEEP_M)]) * n_copies
+    log(f"weight copies resident: {resident / 1e6:.0f} MB")
     step_bytes = sum(algorithmic_bytes(c["n"], c["k"]) for c in calls)
 
     # ---------------------------------------------------------------- graphs
     cap = torch.cuda.Stream()
-    # eager run once on the capture stream: checks every call is accepted and
-    # sets up the library's split-K workspace of that stream outside capture
-    for c in calls:
+    for c in calls:  # eager run on the capture stream: every call is accepted
         launch(c, 0, cap.cuda_stream)
     torch.cuda.synchronize()
     graphs = []
@@ -206,14 +288,13 @@ def main() -> int:
     log(f"{args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_ms * 1e3 / args.steps:.2f} us/step events")
 
     # ---------------------------------------------------------------- per call
-    per_call = []
-    L = args.per_call_launches
-    for c in calls:
+    def time_graph(launch_i, n_launch: int) -> float:
+        """µs per launch of a graph of n_launch launches, HIP events on the replay stream."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             h = torch.cuda.current_stream().cuda_stream
-            for i in range(L):
-                launch(c, i % (COPY_SETS * len(SWEEP_M)), h)
+            for i in range(n_launch):
+                launch_i(i, h)
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -223,13 +304,18 @@ def main() -> int:
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (reps * L)
+        del g
+        return a.elapsed_time(b) * 1e3 / (reps * n_launch)
+
+    per_call = []
+    L = args.per_call_launches
+    for c in calls:
+        us = time_graph(lambda i, h, c=c: launch(c, i % n_copies, h), L)
         nbytes = algorithmic_bytes(c["n"], c["k"])
-        per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": kernel_name(c["m"], c["k"]),
+        per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": c["kernel"],
                          "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                          "frac_peak": round(nbytes / us / 1e3 / PEAK_GBPS, 4), "bytes": nbytes})
-        log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s")
-        del g
+        log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s  {c['kernel']}")
 
     # dominant kernel: largest share of the step's time
     share = {}
@@ -247,7 +333,14 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": dom, "avg_us_per_launch": round(avg_us, 3),
-                "algorithmic_bytes_per_launch": int(avg_bytes), "launches_per_step": d["launches"]}
+                "algorithmic_bytes_per_launch": int(avg_bytes), "launches_per_step": d["launches"],
+                "step_time_share": round(d["us"] / sum(pc["us"] for pc in per_call), 3)}
+    del graphs
+    for c in calls:
+        c["w"] = c["s"] = None
+    torch.cuda.empty_cache()
+
+    extras = [] if args.no_extras else run_extras(torch, dev, lib, cap, time_graph)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -275,10 +368,94 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_call": per_call,
+        "extras": extras,
         "source_digest": source_digest(),
     }
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def run_extras(torch, dev, lib, cap, time_graph) -> list:
+    """Per-call timings of the other workloads (not part of the step)."""
+    import synth
+    from w4a16_nvfp4_gemv_amd import gemv_kernel_name, moe_down_combine, moe_gate_up
+
+    out = []
+    budget = 600e6  # bytes of rotating weight copies per shape
+
+    # fused gate|up SiLU GEMV, N = 2 x 14336, K = 4096
+    n, k = 2 * 14336, 4096
+    base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(2, 1))
+    nc = max(2, int(budget // (n * k // 2)))
+    ws = [base["w"].to(dev) for _ in range(nc)]
+    ss = [base["s"].to(dev) for _ in range(nc)]
+    for m in (1, 8, 32):
+        d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m))
+        x, gs = d["x"].to(dev), d["gs"].to(dev)
+        o = torch.empty((m, n // 2), dtype=torch.bfloat16, device=dev)
+
+        def f(i, h, m=m, x=x, gs=gs, o=o):
+            assert lib.nvfp4_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), ss[i % nc].data_ptr(),
+                                  gs.data_ptr(), n, 1, o.data_ptr(), h) == 0
+        us = time_graph(f, 32)
+        nb = algorithmic_bytes(n, k)
+        out.append({"workload": "nvfp4_gemv silu_mul", "N": n, "K": k, "M": m, "kernel": gemv_kernel_name(m, n, k, True),
+                    "us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb})
+        log(f"silu N={n} K={k} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s")
+    del ws, ss
+
+    # BF16-weight GEMV
+    for n, k in ((4096, 4096), (4096, 14336)):
+        base = synth.dense_bf16(1, n, k, seed=synth.seed_for(3, 1, k))
+        nc = max(2, int(budget // (n * k * 2)))
+        ws = [base["w"].to(dev) for _ in range(nc)]
+        for m in (1, 4, 16, 32):
+            d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m, k))
+            x = d["x"].to(dev)
+            o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+            def f(i, h, m=m, x=x, o=o, n=n, k=k):
+                assert lib.bf16_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), n, 0, o.data_ptr(), h) == 0
+            us = time_graph(f, 32)
+            nb = n * k * 2
+            out.append({"workload": "bf16_gemv", "N": n, "K": k, "M": m,
+                        "kernel": gemv_kernel_name(m, n, k, weight_fp4=False),
+                        "us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb})
+            log(f"bf16 N={n} K={k} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s")
+        del ws
+
+    # MoE decode pair: 128 experts, top-8, H = 4096, I = SI = 1536
+    E, T, H, I, SI = synth.MOE_EXPERTS, synth.MOE_TOPK, synth.MOE_HIDDEN, synth.MOE_INTER, synth.MOE_SHARED_INTER
+    wts = {k2: v.to(dev) for k2, v in synth.moe_weights(E, H, I, SI, seed=synth.seed_for(4, 0)).items()}
+    w1_e = 2 * I * H // 2 + synth.flat_scale_bytes(2 * I, H)
+    w2_e = H * I // 2 + synth.flat_scale_bytes(H, I)
+    sh1 = 2 * SI * H // 2 + synth.flat_scale_bytes(2 * SI, H)
+    sh2 = H * SI // 2 + synth.flat_scale_bytes(H, SI)
+    for m in (1, 8, 32):
+        sets = []
+        for r in range(16):  # rotating routings: fresh experts every launch
+            tk = synth.moe_tokens(m, H, E, T, seed=synth.seed_for(4, m, r))
+            sets.append({k2: v.to(dev) for k2, v in tk.items()})
+        act = torch.empty((m * T, I), dtype=torch.bfloat16, device=dev)
+        sact = torch.empty((m, SI), dtype=torch.bfloat16, device=dev)
+        o = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+
+        def gu(i, h, sets=sets, act=act, sact=sact):
+            t = sets[i % len(sets)]
+            moe_gate_up(t["x"], t["ids"], wts["w1"], wts["w1_sf"], wts["alpha"], act, wts["wsh"], wts["ssh"],
+                        wts["gssh"], sact)
+
+        def dc(i, h, sets=sets, act=act, sact=sact, o=o):
+            t = sets[i % len(sets)]
+            moe_down_combine(act, t["ids"], t["tw"], wts["w2"], wts["w2_sf"], wts["alpha2"], sact, wts["wsd"],
+                             wts["ssd"], wts["gssd"], o)
+        distinct = sum(len(set(t["ids"].flatten().tolist())) for t in sets) / len(sets)
+        for name, fn, nb in (("moe_gate_up", gu, distinct * w1_e + sh1), ("moe_down_combine", dc, distinct * w2_e + sh2)):
+            us = time_graph(fn, 32)
+            out.append({"workload": name, "M": m, "experts_per_call": round(distinct, 2), "us": round(us, 3),
+                        "GBps": round(nb / us / 1e3, 1), "bytes": int(nb)})
+            log(f"{name} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s ({distinct:.1f} experts)")
+    return out
 
 
 if __name__ == "__main__":

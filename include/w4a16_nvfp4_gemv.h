@@ -151,6 +151,17 @@ int moe_down_combine(const uint16_t *act, const int32_t *ids, const float *tw, i
                      const uint8_t *wsd, const uint8_t *ssd, const float *gssd, int64_t SI,
                      uint16_t *out, void *stream);
 
+/*
+ * w4a16_gemv_kernel_name -- host-only query, enqueues nothing: the name of
+ * the kernel instantiation (as profilers print it, without the namespace and
+ * parameter list) that nvfp4_gemv (weight_fp4 = 1) or bf16_gemv
+ * (weight_fp4 = 0) launches for these sizes and silu_mul, under the current
+ * W4A16_GEMV_PATH setting.  Returns "" and records the reason in
+ * w4a16_last_error() for sizes the entry point would reject or for M = 0.
+ * The string lives in static per-thread storage until the next call.
+ */
+const char *w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul);
+
 /* Human-readable name of a status code (static storage). */
 const char *w4a16_status_string(int status);
 

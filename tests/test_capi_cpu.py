@@ -129,3 +129,21 @@ def test_moe_argument_errors():
     assert dc(tw=None) == INVALID
     assert dc(act=FAKE + 8) == MISALIGNED
     assert dc(M=0, act=None) == OK
+
+
+def test_gemv_kernel_name_query(monkeypatch):
+    """The host-only query names the kernel family each dense sweep shape
+    dispatches to, and rejects what the entry points reject."""
+    from w4a16_nvfp4_gemv_amd import W4A16Error, gemv_kernel_name
+    monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
+    for m in (1, 2, 4):
+        assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_vchunk<{m}, false,")
+        assert gemv_kernel_name(m, 28672, 4096, silu_mul=True).startswith(f"k_gemv_vchunk<{m}, true,")
+    for m, nt in ((8, 1), (16, 1), (32, 2)):
+        assert gemv_kernel_name(m, 6144, 4096) == f"k_gemv_mfma<true, {nt}, false>"
+    assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False) == "k_gemv_mfma<false, 2, false>"
+    monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")
+    assert gemv_kernel_name(1, 4096, 4096) == "k_gemv_mfma<true, 1, false>"
+    for bad in (dict(m=0, n=16, k=64), dict(m=33, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
+        with pytest.raises(W4A16Error):
+            gemv_kernel_name(bad["m"], bad["n"], bad["k"])

@@ -122,8 +122,22 @@ def test_nvfp4_gemv_small_shapes(m, n, k, gemv_path):
 
 
 @pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 32])
+@pytest.mark.parametrize("n,k", [(48, 8192), (32, 14336), (144, 16384), (16, 16448), (32, 20480)])
+def test_nvfp4_gemv_long_rows(m, n, k, gemv_path):
+    """Rows past 4096 columns: the chunked VALU kernel with 2-4 K slices and
+    partly empty chunk slots (up to 16384), the LDS-staged VALU kernel beyond,
+    and the MFMA kernel with several steps per wave."""
+    _say("nvfp4_gemv long", m, n, k, gemv_path)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k)
+    got = run_nvfp4(d, n)
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
-@pytest.mark.parametrize("n,k", [(256, 512), (96, 128), (288, 256), (512, 1536)])
+@pytest.mark.parametrize("n,k", [(256, 512), (96, 128), (288, 256), (512, 1536), (64, 12288)])
 def test_nvfp4_gemv_silu_small_shapes(m, n, k, gemv_path):
     _say("nvfp4_gemv silu", m, n, k, gemv_path)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m) + n + k)

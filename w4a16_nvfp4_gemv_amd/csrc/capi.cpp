@@ -127,6 +127,34 @@ int bf16_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16
   return hip_status(w4a16::launch_gemv(false, p, silu_mul, path, static_cast<hipStream_t>(stream)));
 }
 
+const char* w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul) {
+  thread_local char name[128];
+  name[0] = 0;
+  if (weight_fp4 != 0 && weight_fp4 != 1) {
+    fail(W4A16_ERR_INVALID_ARG, "weight_fp4=%lld must be 0 or 1", weight_fp4);
+    return name;
+  }
+  // the size checks of the GEMV entry points, on stand-in aligned pointers
+  const uint16_t* stand_in = reinterpret_cast<const uint16_t*>(uintptr_t(256));
+  const int st = check_dense(stand_in, M, K, K, stand_in, N, silu_mul, reinterpret_cast<uint16_t*>(uintptr_t(256)),
+                             weight_fp4 ? 64 : 16);
+  if (st != W4A16_OK) return name;
+  if (M == 0) {
+    fail(W4A16_ERR_INVALID_ARG, "M=0 launches no kernel");
+    return name;
+  }
+  w4a16::GemvParams p{};
+  p.ldx = K;
+  p.M = static_cast<int>(M);
+  p.N = static_cast<int>(N);
+  p.K = static_cast<int>(K);
+  p.half = silu_mul ? static_cast<int>(N / 2) : 0;
+  const bool fp4 = weight_fp4 != 0;
+  w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, M, N, K), name, sizeof name);
+  ok();
+  return name;
+}
+
 int dequantize_rows(const uint8_t* w, const uint8_t* w_scale, int64_t rows, int64_t K,
                     uint16_t* out, void* stream) {
   if (rows < 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes rows=%lld K=%lld", rows, K);

@@ -1,16 +1,21 @@
 // Dense small-M GEMV kernels for gfx950: out = bf16(fp32(x @ W^T) * gs).
 //
-// Two kernel families serve the same entry points:
-//   * k_gemv_valu  -- VALU dot path for the smallest M.  Lanes split K, every
-//     lane keeps FP32 partial sums for all rows of its unit and all tokens,
-//     and the lane group is reduced with cross-lane adds.  Weights are
-//     dequantized exactly to BF16 pairs and consumed by v_dot2_f32_bf16.
-//   * k_gemv_mfma  -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
+// Three kernel families serve the same entry points:
+//   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns and M <= 4 tokens.
+//     VALU dot products over exactly decoded BF16 pairs (v_dot2_f32_bf16);
+//     lanes own interleaved 8-k chunks so that every load instruction of a
+//     wave reads one contiguous stretch, and a permlane reduce-scatter sums
+//     the lanes.
+//   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
+//     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 and
+//     NVFP4 rows longer than 16384 columns at M <= 2.
+//   * k_gemv_mfma -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
 //     weight rows of a tile are the A operand, up to 16 tokens the B operand.
-//     The four waves of a workgroup split K and reduce through LDS.
-// Both stream every weight byte exactly once with 16-byte loads, and both
-// apply the FP32 global scale to the FP32 sum before the single BF16 rounding
-// (nvfp4_gemv page, module docstring "Numerics").
+//     The waves of a workgroup split K and reduce through LDS.
+// All of them stream every weight byte exactly once with buffer loads, and
+// all apply the FP32 global scale to the FP32 sum before the single BF16
+// rounding (nvfp4_gemv page, module docstring "Numerics").
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // in-order wait for a step's x never waits behind the HBM stream, and every
 // ring iteration issues the same loads (steps past the wave's share read
 // zeros through out-of-range offsets), which keeps the waits exact.
-constexpr int kMfmaWaves = 8;
+constexpr int kMfmaWaves = 4;
 
 template <bool FP4>
 __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
@@ -584,6 +589,13 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
 // ------------------------------------------------------------------ launch
 namespace {
 
+// When set, the launchers below write the name of the kernel they would
+// launch here and launch nothing (describe_gemv).
+thread_local char* t_describe = nullptr;
+thread_local size_t t_describe_len = 0;
+
+const char* tf(bool v) { return v ? "true" : "false"; }
+
 int lanes_per_unit(int64_t tiles) {
   if (tiles > 32) return 64;
   if (tiles > 16) return 32;
@@ -598,6 +610,11 @@ hipError_t launch_valu_lpq(const GemvParams& p, hipStream_t stream) {
   int64_t blocks = (waves + 3) / 4;
   if (blocks > 1024) blocks = 1024;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (t_describe) {
+    if (p.tiles <= LPQ) std::snprintf(t_describe, t_describe_len, "k_gemv_valu1<%s, %d, %d, %s>", tf(FP4), MT, LPQ, tf(SILU));
+    else std::snprintf(t_describe, t_describe_len, "k_gemv_valu<%s, %d, %d, %s, false>", tf(FP4), MT, LPQ, tf(SILU));
+    return hipSuccess;
+  }
   if (p.tiles <= LPQ) {  // one tile per lane: one unit per wave-slot, straight-line kernel
     const dim3 grid1(static_cast<unsigned>((waves + 3) / 4));
     hipLaunchKernelGGL((k_gemv_valu1<FP4, MT, LPQ, SILU>), grid1, block, 0, stream, p);
@@ -611,6 +628,10 @@ hipError_t launch_valu_lpq(const GemvParams& p, hipStream_t stream) {
 template <int MT, bool SILU, int C, int KS>
 hipError_t launch_vchunk_c(const GemvParams& p, hipStream_t stream) {
   constexpr int upb = 4 / KS;
+  if (t_describe) {
+    std::snprintf(t_describe, t_describe_len, "k_gemv_vchunk<%d, %s, %d, %d>", MT, tf(SILU), C, KS);
+    return hipSuccess;
+  }
   const dim3 grid(static_cast<unsigned>((p.units + upb - 1) / upb)), block(256);
   hipLaunchKernelGGL((k_gemv_vchunk<MT, SILU, C, KS>), grid, block, 0, stream, p);
   return hipGetLastError();
@@ -667,6 +688,10 @@ template <bool FP4, int NT, bool SILU>
 hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   p.units = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  if (t_describe) {
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s>", tf(FP4), NT, tf(SILU));
+    return hipSuccess;
+  }
   int64_t blocks = p.units;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)),
@@ -713,6 +738,15 @@ int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K) {
   }
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : 1;
   return (valu_fits && M <= valu_max_m) ? kPathValu : kPathMfma;
+}
+
+void describe_gemv(bool fp4, const GemvParams& p, int silu, int path, char* name, size_t len) {
+  name[0] = 0;
+  t_describe = name;
+  t_describe_len = len;
+  (void)launch_gemv(fp4, p, silu, path, nullptr);
+  t_describe = nullptr;
+  t_describe_len = 0;
 }
 
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream) {

@@ -28,6 +28,9 @@ struct GemvParams {
 
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream);
+// Runs the GEMV dispatch without launching: writes the name of the kernel
+// instantiation launch_gemv would launch for these sizes into name.
+void describe_gemv(bool fp4, const GemvParams& p, int silu, int path, char* name, size_t len);
 
 hipError_t launch_dequantize_rows(const uint8_t* w, const uint8_t* s, int64_t rows, int64_t K,
                                   uint16_t* out, hipStream_t stream);

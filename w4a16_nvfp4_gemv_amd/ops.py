@@ -110,6 +110,16 @@ def nvfp4_unswizzle_scales(weight_scale: torch.Tensor, n: int, k: int) -> torch.
     return out
 
 
+def gemv_kernel_name(m: int, n: int, k: int, silu_mul: bool = False, weight_fp4: bool = True) -> str:
+    """Name of the kernel nvfp4_gemv (or bf16_gemv) launches for these sizes
+    (host-only query; raises W4A16Error for sizes the entry point rejects)."""
+    lib = _lib.load()
+    name = lib.w4a16_gemv_kernel_name(int(weight_fp4), m, n, k, int(silu_mul)).decode()
+    if not name:
+        raise W4A16Error(1, "gemv_kernel_name")
+    return name
+
+
 def moe_gate_up(x, ids, w1, w1_sf, alpha, act, wsh, ssh, gssh, sact) -> None:
     """act[p] = silu(g) * u of the routed experts, sact[t] of the shared one (in place)."""
     x = _x2d(x)
