@@ -203,10 +203,11 @@ int moe_gate_up(const uint16_t* x, int64_t M, int64_t H, const int32_t* ids, int
   p.sact = sact;
   p.w1_expert_bytes = 2 * I * (H / 2);
   p.s1_expert_bytes = flat_scale_bytes(2 * I, H);
-  p.units_per_pair = (I + 127) / 128 * 32;
-  p.units_per_token = (SI + 127) / 128 * 32;
-  p.routed_units = M * topk * p.units_per_pair;
-  p.shared_units = M * p.units_per_token;
+  p.wsh_bytes = 2 * SI * (H / 2);
+  p.ssh_bytes = flat_scale_bytes(2 * SI, H);
+  if (p.w1_expert_bytes > kMaxDim || p.s1_expert_bytes > kMaxDim || p.wsh_bytes > kMaxDim ||
+      M * H * 2 > kMaxDim || M * topk * I * 2 > kMaxDim)
+    return fail(W4A16_ERR_UNSUPPORTED, "per-expert weights and activations must stay below 2 GiB (H=%lld I=%lld)", H, I);
   p.M = static_cast<int>(M);
   p.H = static_cast<int>(H);
   p.topk = static_cast<int>(topk);
@@ -246,8 +247,11 @@ int moe_down_combine(const uint16_t* act, const int32_t* ids, const float* tw, i
   p.out = out;
   p.w2_expert_bytes = H * (I / 2);
   p.s2_expert_bytes = flat_scale_bytes(H, I);
-  p.units_per_token = (H + 127) / 128 * 32;
-  p.units = M * p.units_per_token;
+  p.wsd_bytes = H * (SI / 2);
+  p.ssd_bytes = flat_scale_bytes(H, SI);
+  if (p.w2_expert_bytes > kMaxDim || p.s2_expert_bytes > kMaxDim || p.wsd_bytes > kMaxDim ||
+      M * topk * I * 2 > kMaxDim || M * SI * 2 > kMaxDim)
+    return fail(W4A16_ERR_UNSUPPORTED, "per-expert weights and activations must stay below 2 GiB (H=%lld I=%lld)", H, I);
   p.M = static_cast<int>(M);
   p.topk = static_cast<int>(topk);
   p.E = static_cast<int>(E);

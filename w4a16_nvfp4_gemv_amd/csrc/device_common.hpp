@@ -105,6 +105,13 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+// `v` when `cond` holds, else an offset at or above kOutOfRange (v < 2^31).
+// Plain bit arithmetic: unlike a ?: or && the compiler cannot turn it into a
+// branch around the load that uses it.
+__device__ __forceinline__ uint32_t off_if(bool cond, uint32_t v) {
+  return v | (static_cast<uint32_t>(!cond) << 31);
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }

@@ -48,9 +48,9 @@ struct MoeGateUpParams {
   const uint8_t* ssh;
   const float* gssh;      // [1]
   uint16_t* sact;         // [M][SI]
-  int64_t w1_expert_bytes, s1_expert_bytes;
-  int64_t routed_units, shared_units, units_per_pair, units_per_token;
+  int64_t w1_expert_bytes, s1_expert_bytes, wsh_bytes, ssh_bytes;
   int M, H, topk, E, I, SI;
+  int slots_max;          // min(M * topk, E): workgroup rows of routed experts
 };
 
 struct MoeDownParams {
@@ -65,8 +65,7 @@ struct MoeDownParams {
   const uint8_t* ssd;
   const float* gssd;      // [1]
   uint16_t* out;          // [M][H]
-  int64_t w2_expert_bytes, s2_expert_bytes;
-  int64_t units_per_token, units;
+  int64_t w2_expert_bytes, s2_expert_bytes, wsd_bytes, ssd_bytes;
   int M, topk, E, H, I, SI;
 };
 

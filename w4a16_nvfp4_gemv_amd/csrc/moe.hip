@@ -1,213 +1,525 @@
-// Expert-indexed MoE decode pair (moe_gemv page): gate_up, then
-// down_combine, both built from the VALU unit of the dense GEMV.
+// Expert-indexed MoE decode pair (moe_gemv page, module docstring and the
+// gate_up / down_combine docstrings), expert-major: every routed expert's
+// weights are read once per call, for all the tokens routed to it.
 //
-// gate_up: one unit per (routed pair p, gate quad) and per (token, shared
-// gate quad).  A unit reads the gate quad and the matching up quad (rows i and
-// I + i of the expert's [gate; up] weight) over the whole hidden size and
-// writes act[p][i] = bf16(silu(g) * u) with g, u = FP32 accumulator * alpha[e]
-// (routed), or sact[t][i] = bf16(silu(bf16(g)) * bf16(u)) (shared expert, the
-// dense silu_mul numerics).
+// Routing.  Every workgroup rebuilds the call's routing in LDS from ids (at
+// most 32 tokens x 16 slots = 512 pairs): the distinct experts in order of
+// first appearance ("slots"), and the pairs of every slot in ascending pair
+// order.  No host synchronization and no workspace are needed, and the order
+// of every floating-point sum depends on ids alone.
 //
-// down_combine: one workgroup per (token, quad of output rows).  Its lane
-// groups compute the topk routed down projections and the shared one at the
-// same time (each over the whole intermediate size); the per-piece results
-// meet in LDS, where the FP32 weighted sum is formed over j ascending and
-// out = bf16(bf16(sum_j tw_j * y_j) + y_shared) is written.
+// gate_up.  One workgroup per gate quad of the routed experts' I rows and
+// per gate quad of the shared expert's SI rows.  A routed workgroup walks the
+// slots: for each, its four waves split the hidden size H of the expert's
+// gate and up quads (chunk-interleaved loads, chunk_core.hpp), meet in LDS,
+// and the results of the slot's tokens are kept in LDS; they are stored once
+// the walk is over.
+//   routed: act[p][i] = bf16(silu(g) * u),  g, u = FP32 sum * alpha[e]
+//   shared: sact[t][i] = bf16(silu(bf16(g)) * bf16(u)),  g, u = FP32 sum * gssh
+//
+// down_combine.  One workgroup per quad of the H output rows.  Its waves take
+// the slots round robin (slot D being the shared expert); for every token of
+// a slot the wave forms y = bf16(FP32 sum * alpha2[e]) and adds tw * y to its
+// own FP32 partial of that token in LDS.  The four partials are added in wave
+// order, then out = bf16(bf16(sum) + y_shared).
+//
+// Both kernels stream their jobs (slot, group of tokens, K block) through a
+// two-slot ring of registers: a slot is consumed, then refilled in place with
+// the job two ahead, so one job's loads are in flight while the other is
+// computed.  No global store and no other vector load happens inside the
+// ring: vmcnt waits are in order, and a store or a late load among the loads
+// in flight would make every wait drain the ring.
+#include "chunk_core.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "unit_core.hpp"
 
 namespace w4a16 {
 
-__device__ __forceinline__ int64_t clamp_expert(int32_t id, int E) {
+constexpr int kMoeMaxPairs = 512;  // 32 tokens x 16 slots
+constexpr int kMoeMaxTokens = 32;
+
+__device__ __forceinline__ int clamp_expert(int32_t id, int E) {
   return id < 0 ? 0 : (id >= E ? E - 1 : id);
 }
 
-template <int LPQ>
-__global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
-  constexpr int G = kWave / LPQ;
-  const int lane = threadIdx.x & 63;
-  const int li = lane % LPQ;
-  const int slot = lane / LPQ;
-  const int wave = threadIdx.x >> 6;
-  const int64_t gwave = static_cast<int64_t>(xcd_logical_block()) * 4 + wave;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4 * G;
-  const int64_t total = p.routed_units + p.shared_units;
-  const int64_t row_bytes = p.H / 2;
-  const int64_t tiles = p.H / 64;
+// Values the whole wave agrees on, moved to scalar registers (the compiler
+// cannot always prove that values read from LDS are uniform, and a buffer
+// resource built from a value it deems divergent becomes a per-lane loop).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  return make_rsrc(uniform_ptr(base), __builtin_amdgcn_readfirstlane(bytes));
+}
 
-  for (int64_t ubase = gwave * G; ubase < total; ubase += stride) {
-    const int64_t u = ubase + slot;
-    const bool active = u < total;
-    const bool routed = u < p.routed_units;
-    const uint8_t* w;
-    const uint8_t* s;
-    int64_t t, q, half, dst_base;
-    float scale;
-    uint16_t* dst;
-    if (routed) {
-      const int64_t pair = u / p.units_per_pair;
-      q = u - pair * p.units_per_pair;
-      t = pair / p.topk;
-      const int64_t e = clamp_expert(p.ids[pair], p.E);
-      w = p.w1 + e * p.w1_expert_bytes;
-      s = p.w1s + e * p.s1_expert_bytes;
-      half = p.I;
-      scale = p.alpha[e];
-      dst = p.act;
-      dst_base = pair * p.I;
-    } else {
-      const int64_t v = active ? u - p.routed_units : 0;
-      t = v / p.units_per_token;
-      q = v - t * p.units_per_token;
-      w = p.wsh;
-      s = p.ssh;
-      half = p.SI;
-      scale = *p.gssh;
-      dst = p.sact;
-      dst_base = t * p.SI;
+constexpr int kMoeExpertTable = 2048;  // experts with an LDS first-pair entry
+
+struct alignas(16) MoeRouting {
+  int32_t id[kMoeMaxPairs];         // clamped expert of every pair (-1 past P)
+  int32_t first[kMoeMaxPairs];      // pair -> first pair routed to the same expert
+  int32_t within[kMoeMaxPairs];     // pair -> rank among that expert's pairs
+  int32_t fslot[kMoeMaxPairs];      // first pair -> its slot
+  int32_t expert[kMoeMaxPairs];     // slot -> expert
+  int32_t count[kMoeMaxPairs];      // slot -> number of pairs
+  int32_t start[kMoeMaxPairs + 1];  // slot -> offset into order
+  int32_t order[kMoeMaxPairs];      // pairs grouped by slot, ascending within a slot
+  float tw[kMoeMaxPairs];           // pair -> routing weight (down_combine)
+  int32_t first_of[kMoeExpertTable];  // expert -> first pair (E <= kMoeExpertTable)
+  int32_t chunk_firsts[kMoeMaxPairs / 64];
+  int32_t D;                        // distinct experts
+};
+
+// Number of i in [lo, hi) with a[i] == v: a scan of an LDS array in blocks of
+// 16 entries read as four 16-byte broadcasts (the array is readable up to
+// kMoeMaxPairs; entries outside [lo, hi) are masked).
+__device__ __forceinline__ int count_equal(const int32_t* a, int lo, int hi, int v) {
+  int n = 0;
+  for (int b = lo & ~15; b < hi; b += 16) {
+    const int4* q = reinterpret_cast<const int4*>(a + b);
+    const int4 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
+    const int e[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                       x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) n += (b + k >= lo && b + k < hi && e[k] == v) ? 1 : 0;
+  }
+  return n;
+}
+
+// Sum of a[0..hi) (same blocked reads).
+__device__ __forceinline__ int sum_prefix(const int32_t* a, int hi) {
+  int n = 0;
+  for (int b = 0; b < hi; b += 16) {
+    const int4* q = reinterpret_cast<const int4*>(a + b);
+    const int4 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
+    const int e[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                       x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) n += (b + k < hi) ? e[k] : 0;
+  }
+  return n;
+}
+
+// Builds the routing of P pairs with the whole workgroup; tw (may be null)
+// is loaded together with ids.  Ends with a barrier.
+//   first pair of every expert: an atomicMin per pair into an LDS table (E up
+//     to kMoeExpertTable; larger E falls back to a scan of the earlier pairs);
+//   slot of a first pair: number of first pairs before it, from 64-pair
+//     ballots; within-expert rank: number of earlier pairs with that expert.
+__device__ void build_routing(MoeRouting& r, const int32_t* ids, const float* tw, int P, int E) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nt >> 6;
+  const bool table = E <= kMoeExpertTable;
+  if (table)
+    for (int e = tid; e < E; e += nt) r.first_of[e] = kMoeMaxPairs;
+  for (int p = tid; p < kMoeMaxPairs; p += nt) {
+    r.id[p] = p < P ? clamp_expert(ids[p], E) : -1;
+    if (tw && p < P) r.tw[p] = tw[p];
+    r.count[p] = 0;
+  }
+  __syncthreads();
+  if (table)
+    for (int p = tid; p < P; p += nt) atomicMin(&r.first_of[r.id[p]], p);
+  __syncthreads();
+  for (int p = tid; p < P; p += nt) {
+    const int e = r.id[p];
+    const int within = count_equal(r.id, 0, p, e);
+    int first = p;
+    if (table) {
+      first = r.first_of[e];
+    } else if (within > 0) {
+      for (int q = 0; q < p; ++q) {
+        if (r.id[q] == e) {
+          first = q;
+          break;
+        }
+      }
     }
+    r.first[p] = first;
+    r.within[p] = within;
+  }
+  __syncthreads();
+  // slots: ranks of the first pairs, chunk by chunk of 64 pairs
+  const int nchunks = (P + 63) / 64;
+  for (int c = wave; c < nchunks; c += nwaves) {
+    const int p = c * 64 + lane;
+    const bool f = p < P && r.first[p] == p;
+    const uint64_t mask = __ballot(f);
+    if (lane == 0) r.chunk_firsts[c] = __popcll(mask);
+  }
+  __syncthreads();
+  for (int c = wave; c < nchunks; c += nwaves) {
+    const int p = c * 64 + lane;
+    const bool f = p < P && r.first[p] == p;
+    const uint64_t mask = __ballot(f);
+    int before = __popcll(mask & ((uint64_t(1) << lane) - 1));
+    for (int c2 = 0; c2 < c; ++c2) before += r.chunk_firsts[c2];
+    if (f) {
+      r.fslot[p] = before;
+      r.expert[before] = r.id[p];
+    }
+  }
+  if (tid == 0) {
+    int d = 0;
+    for (int c = 0; c < nchunks; ++c) d += r.chunk_firsts[c];
+    r.D = d;
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += nt) atomicAdd(&r.count[r.fslot[r.first[p]]], 1);
+  __syncthreads();
+  const int D = r.D;
+  for (int s = tid; s <= D; s += nt) r.start[s] = sum_prefix(r.count, s);
+  __syncthreads();
+  for (int p = tid; p < P; p += nt) r.order[r.start[r.fslot[r.first[p]]] + r.within[p]] = p;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ gate_up
+// Work items are (slot, gate quad of the expert's I rows) and (gate quad of
+// the shared expert's SI rows); a persistent grid builds the routing once per
+// workgroup and walks the items.  For an item, the four waves split H; the
+// expert's gate and up quads are read once (per K block) and applied to the
+// slot's tokens MT at a time.  Each item is straight-line: all of its loads
+// are issued before its arithmetic, and its results are stored before the
+// next item's loads (so no wait ever mixes stores and loads in flight).
+template <int MT, int C>
+__global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
+  constexpr int KS = 4;                 // waves per item, each a slice of H
+  constexpr int PV = 2;                 // gate, up
+  constexpr int V = MT * 4 * PV;        // value index (m * 4 + q) * 2 + u
+  using RS = ReduceScatter<V, PV>;
+  __shared__ MoeRouting rt;
+  __shared__ float red[KS - 1][RS::LEFT][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int kw = uniform(tid >> 6);
+  const int P = p.M * p.topk;
+  build_routing(rt, p.ids, nullptr, P, p.E);
+  const int D = uniform(rt.D);
+  // 32-bit item bookkeeping: at most 512 slots x (I / 4) quads
+  const int units_r = (p.I + 127) / 128 * 32;
+  const int units_s = (p.SI + 127) / 128 * 32;
+  const int items = D * units_r + units_s;
+  const uint32_t nch = p.H / 8;
+  const int nkb = static_cast<int>((nch + KS * C * 64 - 1) / (KS * C * 64));
+  const uint32_t shift = 8u * ((lane >> 1) & 3);
+  const uint32_t row_bytes = p.H / 2;
+  const uint32_t tiles = p.H / 64;
+  const rsrc_t rx = make_rsrc(p.x, static_cast<uint32_t>(p.M) * p.H * 2);
+  const float gssh = *p.gssh;
+
+  for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
+    const bool shared = item >= D * units_r;
+    const int s = shared ? 0 : item / units_r;
+    const int u = shared ? item - D * units_r : item - s * units_r;
+    const int e = shared ? 0 : uniform(rt.expert[s]);
+    const int cnt = shared ? p.M : uniform(rt.count[s]);
+    const int first = shared ? 0 : uniform(rt.start[s]);
+    const int half = shared ? p.SI : p.I;
+    const float scale = shared ? gssh : p.alpha[e];
     int64_t rows[8];
     bool rv[8];
-    quad_rows<8>(q, half, half, rows, rv);
-    if (!active) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rv[i] = false;
-    }
+    quad_rows<8>(u, half, half, rows, rv);
     const bool quad_ok[2] = {true, half % 128 == 0};
-    float acc[8][1];
-    unit_dot<true, 8, 1, LPQ>(w, row_bytes, s, tiles, rows, rv, quad_ok, p.x + t * p.H, p.H, 1,
-                              li, active, acc);
+    const rsrc_t rw = uniform_rsrc(shared ? p.wsh : p.w1 + e * p.w1_expert_bytes,
+                                   static_cast<uint32_t>(shared ? p.wsh_bytes : p.w1_expert_bytes));
+    const rsrc_t rs = uniform_rsrc(shared ? p.ssh : p.w1s + e * p.s1_expert_bytes,
+                                   static_cast<uint32_t>(shared ? p.ssh_bytes : p.s1_expert_bytes));
+
+    for (int g0 = 0; g0 < cnt; g0 += MT) {
+      // token rows of this group (pairs of the slot in ascending order)
+      uint32_t xoff[MT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i % LPQ != li || !rv[i]) continue;
-      float v;
-      if (routed) {
-        const float g = acc[i][0] * scale;
-        const float up = acc[4 + i][0] * scale;
-        v = silu_f32(g) * up;
-      } else {
-        const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][0] * scale));
-        const float up = bf16_bits_to_f32(f32_to_bf16_bits(acc[4 + i][0] * scale));
-        v = silu_f32(g) * up;
+      for (int m = 0; m < MT; ++m) {
+        const int idx = g0 + m;
+        const int t = shared ? idx : rt.order[first + (idx < cnt ? idx : cnt - 1)] / p.topk;
+        xoff[m] = off_if(idx < cnt, static_cast<uint32_t>(t) * p.H * 2);
       }
-      dst[dst_base + rows[i]] = f32_to_bf16_bits(v);
+      float acc[8][MT];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+      for (int kb = 0; kb < nkb; ++kb) {
+        uint32_t ch[C];
+        bool ok[C];
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+          ch[q] = static_cast<uint32_t>((kb * KS + kw) * C + q) * 64 + lane;
+          ok[q] = ch[q] < nch;
+        }
+        ChunkX<C, MT> xb;
+        ChunkW<C, 8> wb;
+        chunk_issue_x<C, MT>(xb, rx, xoff, ch, ok);
+        chunk_issue_w<C, 8>(wb, rw, row_bytes, rs, tiles, rows, rv, quad_ok, ch, ok);
+        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
+        chunk_compute<C, 8, MT>(wb, xb, shift, acc);
+      }
+      float v[V];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int w = 0; w < PV; ++w) v[(m * 4 + q) * PV + w] = acc[4 * w + q][m];
+      reduce_scatter<V, PV>(v);
+      if (kw > 0) {
+#pragma unroll
+        for (int i = 0; i < RS::LEFT; ++i) red[kw - 1][i][lane] = v[i];
+      }
+      __syncthreads();
+      if (kw == 0) {
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+          for (int i = 0; i < RS::LEFT; ++i) v[i] += red[w][i][lane];
+        const int base = reduce_scatter_base<V, PV>(lane);
+#pragma unroll
+        for (int i = 0; i < RS::LEFT / PV; ++i) {
+          const int vi = base + i * PV;
+          const int m = vi / (4 * PV), q = (vi / PV) % 4;
+          const int idx = g0 + m;
+          const int64_t row = static_cast<int64_t>(u >> 5) * 128 + (u & 31) + 32 * q;
+          if ((lane & 15) == i && idx < cnt && row < half) {
+            float g = v[i * PV] * scale, up = v[i * PV + 1] * scale;
+            if (shared) {
+              g = bf16_bits_to_f32(f32_to_bf16_bits(g));
+              up = bf16_bits_to_f32(f32_to_bf16_bits(up));
+              p.sact[static_cast<int64_t>(idx) * p.SI + row] = f32_to_bf16_bits(silu_f32(g) * up);
+            } else {
+              const int pair = rt.order[first + idx];
+              p.act[static_cast<int64_t>(pair) * p.I + row] = f32_to_bf16_bits(silu_f32(g) * up);
+            }
+          }
+        }
+      }
+      __syncthreads();
     }
   }
 }
 
-// One workgroup of `waves` waves per (token, output quad); piece j < topk is
-// routed slot j, piece topk the shared expert.  G pieces per wave.
-template <int LPQ>
-__global__ __launch_bounds__(1024) void k_moe_down_combine(const MoeDownParams p) {
-  constexpr int G = kWave / LPQ;
-  __shared__ float part[17][4];
-  const int lane = threadIdx.x & 63;
-  const int li = lane % LPQ;
-  const int wave = threadIdx.x >> 6;
-  const int piece = wave * G + lane / LPQ;
-  const int pieces = p.topk + 1;
+// ------------------------------------------------------------------ down_combine
+template <int MT, int C>
+__global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p) {
+  constexpr int V = MT * 4;  // value index m * 4 + q
+  using RS = ReduceScatter<V, 1>;
+  __shared__ MoeRouting rt;
+  __shared__ float part[4][kMoeMaxTokens][4];
+  __shared__ float ysh[kMoeMaxTokens][4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int P = p.M * p.topk;
+  build_routing(rt, p.ids, p.tw, P, p.E);
+  const int D = uniform(rt.D);
+  const float gssd = *p.gssd;
+  const int64_t units = (p.H + 127) / 128 * 32;
+  const uint32_t shift = 8u * ((lane >> 1) & 3);
+  const uint32_t act_bytes = static_cast<uint32_t>(P) * p.I * 2;
+  const uint32_t sact_bytes = static_cast<uint32_t>(p.M) * p.SI * 2;
 
-  for (int64_t u = xcd_logical_block(); u < p.units; u += gridDim.x) {
-    const int64_t t = u / p.units_per_token;
-    const int64_t q = u - t * p.units_per_token;
+  // Job = (slot s, group of MT tokens from g0, K block kb); wave w takes the
+  // slots s = w, w + 4, ...; slot D is the shared expert.
+  struct Job {
+    int s, g0, kb;
+  };
+  auto npairs_of = [&](int s) -> int {
+    const int cnt = uniform(rt.count[s < D ? s : D - 1]);
+    return s < D ? cnt : p.M;
+  };
+  auto nkb_of = [&](int s) -> int {
+    const int k = s < D ? p.I : p.SI;
+    return (k / 8 + C * 64 - 1) / (C * 64);
+  };
+  auto advance = [&](Job j) -> Job {
+    if (++j.kb == nkb_of(j.s)) {
+      j.kb = 0;
+      j.g0 += MT;
+      if (j.g0 >= npairs_of(j.s)) {
+        j.g0 = 0;
+        j.s += 4;
+      }
+    }
+    return j;
+  };
+  int njobs = 0;
+  for (int s = wave; s <= D; s += 4) njobs += (npairs_of(s) + MT - 1) / MT * nkb_of(s);
+
+  for (int64_t u = xcd_logical_block(); u < units; u += gridDim.x) {
     int64_t rows[4];
     bool rv[4];
-    quad_rows<4>(q, p.H, 0, rows, rv);
-    const bool active = piece < pieces;
-    const bool routed = piece < p.topk;
-    const uint8_t* w;
-    const uint8_t* s;
-    const uint16_t* xrow;
-    int64_t kdim;
-    float scale, weight;
-    if (routed) {
-      const int64_t pair = t * p.topk + piece;
-      const int64_t e = clamp_expert(p.ids[pair], p.E);
-      w = p.w2 + e * p.w2_expert_bytes;
-      s = p.w2s + e * p.s2_expert_bytes;
-      xrow = p.act + pair * p.I;
-      kdim = p.I;
-      scale = p.alpha2[e];
-      weight = p.tw[pair];
-    } else {
-      w = p.wsd;
-      s = p.ssd;
-      xrow = p.sact + t * p.SI;
-      kdim = p.SI;
-      scale = *p.gssd;
-      weight = 1.0f;
-    }
-    bool rva[4];
+    quad_rows<4>(u, p.H, 0, rows, rv);
+    for (int i = lane; i < p.M * 4; i += 64) part[wave][i >> 2][i & 3] = 0.0f;
+
+    auto issue = [&](const Job& j, ChunkW<C, 4>& wb, ChunkX<C, MT>& xb) {
+      const bool valid = j.s <= D;
+      const bool shared = j.s == D;
+      const int e = uniform(rt.expert[j.s < D ? j.s : D - 1]);
+      const int k = shared ? p.SI : p.I;
+      const uint32_t nch = k / 8;
+      uint32_t ch[C];
+      bool ok[C];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rva[i] = rv[i] && active;
-    const bool quad_ok[1] = {true};
-    float acc[4][1];
-    unit_dot<true, 4, 1, LPQ>(w, kdim / 2, s, kdim / 64, rows, rva, quad_ok, xrow, kdim, 1, li,
-                              active, acc);
-    if (active && li < 4) {
-      float v = li == 0 ? acc[0][0] : li == 1 ? acc[1][0] : li == 2 ? acc[2][0] : acc[3][0];
-      // y = bf16(acc * alpha); routed pieces contribute tw * y (FP32).
-      const float y = bf16_bits_to_f32(f32_to_bf16_bits(v * scale));
-      part[piece][li] = routed ? weight * y : y;
+      for (int q = 0; q < C; ++q) {
+        ch[q] = static_cast<uint32_t>(j.kb * C + q) * 64 + lane;
+        ok[q] = valid && ch[q] < nch;
+      }
+      const int np = valid ? npairs_of(j.s) : 0;
+      const int first = rt.start[j.s < D ? j.s : D];
+      uint32_t xoff[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int idx = j.g0 + m;
+        const int o = first + idx;
+        const int row = shared ? idx : rt.order[o < P ? o : P - 1];
+        xoff[m] = off_if(idx < np, static_cast<uint32_t>(row) * k * 2);
+      }
+      chunk_issue_x<C, MT>(xb, uniform_rsrc(shared ? static_cast<const void*>(p.sact) : static_cast<const void*>(p.act),
+                                            shared ? sact_bytes : act_bytes),
+                           xoff, ch, ok);
+      const bool quad_ok[1] = {true};
+      const uint8_t* wbase = shared ? p.wsd : p.w2 + e * p.w2_expert_bytes;
+      const uint8_t* sbase = shared ? p.ssd : p.w2s + e * p.s2_expert_bytes;
+      const uint32_t wbytes = static_cast<uint32_t>(shared ? p.wsd_bytes : p.w2_expert_bytes);
+      const uint32_t sbytes = static_cast<uint32_t>(shared ? p.ssd_bytes : p.s2_expert_bytes);
+      chunk_issue_w<C, 4>(wb, uniform_rsrc(wbase, wbytes), k / 2, uniform_rsrc(sbase, sbytes), k / 64, rows, rv,
+                          quad_ok, ch, ok);
+      __builtin_amdgcn_sched_barrier(0);  // as in k_moe_gate_up
+    };
+
+    float acc[4][MT];
+    auto finish = [&](const Job& j) {
+      const bool shared = j.s == D;
+      // a scalar load: it does not count against the vector loads in flight
+      const float scale = shared ? gssd : p.alpha2[uniform(rt.expert[j.s < D ? j.s : D - 1])];
+      const int np = npairs_of(j.s);
+      const int first = rt.start[j.s < D ? j.s : D];
+      float v[V];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[m * 4 + q] = acc[q][m];
+      reduce_scatter<V, 1>(v);
+      const int base = reduce_scatter_base<V, 1>(lane);
+      // one token at a time: two pairs of one token routed to the same
+      // expert must not update its partial in the same instruction
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm) {
+#pragma unroll
+        for (int i = 0; i < RS::LEFT; ++i) {
+          const int vi = base + i;
+          const int m = vi / 4, q = vi % 4;
+          const int idx = j.g0 + m;
+          if (m == mm && (lane & 15) == i && idx < np) {
+            const float y = bf16_bits_to_f32(f32_to_bf16_bits(v[i] * scale));
+            if (shared) {
+              ysh[idx][q] = y;
+            } else {
+              const int pair = rt.order[first + idx];
+              part[wave][pair / p.topk][q] += rt.tw[pair] * y;
+            }
+          }
+        }
+      }
+    };
+
+    ChunkW<C, 4> wa, wb;
+    ChunkX<C, MT> xa, xb;
+    Job ja{wave, 0, 0};
+    Job jb = advance(ja);
+    issue(ja, wa, xa);
+    issue(jb, wb, xb);  // jobs past the last slot read nothing
+    auto consume = [&](const Job& j, const ChunkW<C, 4>& w, const ChunkX<C, MT>& x) {
+      if (j.kb == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
+      }
+      chunk_compute<C, 4, MT>(w, x, shift, acc);
+      if (j.kb == nkb_of(j.s) - 1) finish(j);
+    };
+    for (int i = 0; i < njobs; i += 2) {
+      consume(ja, wa, xa);
+      ja = advance(jb);
+      issue(ja, wa, xa);
+      if (i + 1 < njobs) consume(jb, wb, xb);
+      jb = advance(ja);
+      issue(jb, wb, xb);
     }
     __syncthreads();
-    if (threadIdx.x < 4) {
-      const int i = threadIdx.x;
-      float sum = 0.0f;
-      for (int j = 0; j < p.topk; ++j) sum += part[j][i];
-      const float sr = bf16_bits_to_f32(f32_to_bf16_bits(sum));
-      const float v = sr + part[p.topk][i];
-      const int64_t row = rows[i];
-      if (row < p.H) p.out[t * p.H + row] = f32_to_bf16_bits(v);
+    for (int i = tid; i < p.M * 4; i += blockDim.x) {
+      const int t = i >> 2, q = i & 3;
+      const int64_t row = (u >> 5) * 128 + (u & 31) + 32 * q;
+      if (row < p.H) {
+        const float s = ((part[0][t][q] + part[1][t][q]) + part[2][t][q]) + part[3][t][q];
+        const float sr = bf16_bits_to_f32(f32_to_bf16_bits(s));
+        p.out[static_cast<int64_t>(t) * p.H + row] = f32_to_bf16_bits(sr + ysh[t][q]);
+      }
     }
     __syncthreads();
   }
 }
 
+// ------------------------------------------------------------------ launch
 namespace {
-int lanes_for_tiles(int64_t tiles) {
-  if (tiles > 32) return 64;
-  if (tiles > 16) return 32;
-  if (tiles > 8) return 16;
-  return 8;
+
+// Persistent gate_up workgroups: about five resident per CU.
+constexpr int64_t kMoeGateUpGrid = 1280;
+
+template <int MT>
+hipError_t launch_gate_up_mt(const MoeGateUpParams& p, int c, hipStream_t stream) {
+  const int64_t max_items = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 32) + (p.SI + 127) / 128 * 32;
+  const dim3 grid(static_cast<unsigned>(max_items < kMoeGateUpGrid ? max_items : kMoeGateUpGrid)), block(256);
+  switch (c) {
+    case 1: hipLaunchKernelGGL((k_moe_gate_up<MT, 1>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((k_moe_gate_up<MT, 2>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
 }
+
+template <int MT>
+hipError_t launch_down_mt(const MoeDownParams& p, int c, hipStream_t stream) {
+  const int64_t units = (p.H + 127) / 128 * 32;
+  const dim3 grid(static_cast<unsigned>(units < 4096 ? units : 4096)), block(256);
+  switch (c) {
+    case 1: hipLaunchKernelGGL((k_moe_down_combine<MT, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_moe_down_combine<MT, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((k_moe_down_combine<MT, 3>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((k_moe_down_combine<MT, 4>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+// Chunk positions per lane: enough to cover K in one block where that fits
+// in `cmax`, else `cmax` and several K blocks.
+int chunks_per_lane(int64_t k, int64_t lanes, int cmax) {
+  const int64_t need = (k / 8 + lanes - 1) / lanes;
+  if (need <= 1) return 1;
+  if (need <= 2) return 2;
+  if (need <= 3 && cmax >= 3) return 3;
+  return cmax;
+}
+
 }  // namespace
 
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
-  const int lpq = lanes_for_tiles(p.H / 64);
-  const int64_t g = kWave / lpq;
-  const int64_t total = p.routed_units + p.shared_units;
-  const int64_t waves = (total + g - 1) / g;
-  int64_t blocks = (waves + 3) / 4;
-  if (blocks > 16384) blocks = 16384;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  switch (lpq) {
-    case 64: hipLaunchKernelGGL(k_moe_gate_up<64>, grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(k_moe_gate_up<32>, grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(k_moe_gate_up<16>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(k_moe_gate_up<8>, grid, block, 0, stream, p); break;
-  }
-  return hipGetLastError();
+  const int c = chunks_per_lane(p.H, 4 * 64, 2);
+  const int pairs = p.M * p.topk;
+  p.slots_max = pairs < p.E ? pairs : p.E;
+  if (p.M <= 1) return launch_gate_up_mt<1>(p, c, stream);
+  if (p.M <= 8) return launch_gate_up_mt<2>(p, c, stream);
+  return launch_gate_up_mt<4>(p, c, stream);
 }
 
 hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
   const int64_t kmax = p.I > p.SI ? p.I : p.SI;
-  int lpq = lanes_for_tiles(kmax / 64);
-  // at most 16 waves (1024 threads) per workgroup
-  while (lpq > 8 && (p.topk + 1 + kWave / lpq - 1) / (kWave / lpq) > 16) lpq /= 2;
-  const int g = kWave / lpq;
-  const int waves = (p.topk + 1 + g - 1) / g;
-  int64_t blocks = p.units;
-  if (blocks > 65536) blocks = 65536;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * waves);
-  switch (lpq) {
-    case 64: hipLaunchKernelGGL(k_moe_down_combine<64>, grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(k_moe_down_combine<32>, grid, block, 0, stream, p); break;
-    case 16: hipLaunchKernelGGL(k_moe_down_combine<16>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(k_moe_down_combine<8>, grid, block, 0, stream, p); break;
-  }
-  return hipGetLastError();
+  const int c = chunks_per_lane(kmax, 64, 4);
+  return launch_down_mt<1>(p, c, stream);
 }
 
 }  // namespace w4a16
