@@ -15,6 +15,7 @@
 // All of them stream every weight byte exactly once with buffer loads, and
 // all apply the FP32 global scale to the FP32 sum before the single BF16
 // rounding (nvfp4_gemv page, module docstring "Numerics").
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -443,9 +444,9 @@ __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
   else return tile * 16 + r;
 }
 
-template <bool FP4, int NT, bool SILU>
+template <bool FP4, int NT, bool SILU, int RT>
 __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams p) {
-  constexpr int NA = SILU ? 2 : 1;          // A operands per step (gate, up)
+  constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
   constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
   constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
   constexpr int D = FP4 ? 4 : (NT == 1 ? 16 : 8);  // steps in flight per wave
@@ -468,13 +469,17 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
   const float gs = FP4 ? *p.gs : 1.0f;
 
   for (int64_t tile = xcd_logical_block(); tile < p.units; tile += gridDim.x) {
+    // A operand a: row tile tile*RT + a % RT, the up half for a >= RT
     int64_t rows[NA];
     bool rv[NA];
-    rows[0] = mfma_row<FP4>(tile, r);
-    rv[0] = rows[0] < limit;
-    if constexpr (SILU) {
-      rows[1] = rows[0] + p.half;
-      rv[1] = rv[0];
+#pragma unroll
+    for (int a = 0; a < RT; ++a) {
+      rows[a] = mfma_row<FP4>(tile * RT + a, r);
+      rv[a] = rows[a] < limit;
+      if constexpr (SILU) {
+        rows[RT + a] = rows[a] + p.half;
+        rv[RT + a] = rv[a];
+      }
     }
     // x offsets of this lane's B fragments: token 16n + r (bytes), zero past M
     uint32_t xo[NT];
@@ -566,18 +571,21 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
           for (int n = 0; n < NT; ++n) acc[a][n] += red[w][a][n][lane];
       // C layout: lane holds rows 4(l/16)+i of the tile, token column l%16
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int m = 16 * n + (lane & 15);
+      for (int a = 0; a < RT; ++a) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = mfma_row<FP4>(tile, 4 * (lane >> 4) + i);
-          if (m >= p.M || row >= limit) continue;
-          if constexpr (!SILU) {
-            p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(acc[0][n][i] * gs);
-          } else {
-            const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[0][n][i] * gs));
-            const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[1][n][i] * gs));
-            p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+        for (int n = 0; n < NT; ++n) {
+          const int m = 16 * n + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = mfma_row<FP4>(tile * RT + a, 4 * (lane >> 4) + i);
+            if (m >= p.M || row >= limit) continue;
+            if constexpr (!SILU) {
+              p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(acc[a][n][i] * gs);
+            } else {
+              const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[a][n][i] * gs));
+              const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[RT + a][n][i] * gs));
+              p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+            }
           }
         }
       }
@@ -684,19 +692,48 @@ hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
   }
 }
 
-template <bool FP4, int NT, bool SILU>
-hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
+template <bool FP4, int NT, bool SILU, int RT>
+hipError_t launch_mfma_rt(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
-  p.units = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  p.units = (tiles + RT - 1) / RT;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s>", tf(FP4), NT, tf(SILU));
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s, %d>", tf(FP4), NT, tf(SILU), RT);
     return hipSuccess;
   }
   int64_t blocks = p.units;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU, RT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kMfmaWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Row tiles per workgroup.  One tile per workgroup while the tiles fit the
+// compute units in one round; beyond that, two tiles share every activation
+// fragment (half the activation traffic through L2) and the grid keeps one
+// round instead of leaving some units with twice the work of the others.
+int mfma_row_tiles(int64_t tiles) { return tiles > device_cu_count() ? 2 : 1; }
+
+template <bool FP4, int NT, bool SILU>
+hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
+  const int64_t limit = SILU ? p.half : p.N;
+  const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  if (mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, NT, SILU, 2>(p, stream);
+  return launch_mfma_rt<FP4, NT, SILU, 1>(p, stream);
 }
 
 template <bool FP4, bool SILU>
