@@ -135,6 +135,21 @@ def test_nvfp4_gemv_long_rows(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [8, 17, 32])
+@pytest.mark.parametrize("n,k,silu", [(4224, 128, False), (4176, 192, False), (8448, 128, True), (8256, 64, True)])
+def test_nvfp4_gemv_many_row_tiles(m, n, k, silu):
+    """More 16-row tiles than compute units: the MFMA workgroups take two
+    tiles each, including ragged last bands."""
+    _say("nvfp4_gemv many tiles", m, n, k, silu)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k)
+    got = run_nvfp4(d, n, silu=silu)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, d["gs"][0], f"silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 16, 32])
 @pytest.mark.parametrize("n,k", [(256, 512), (96, 128), (288, 256), (512, 1536), (64, 12288)])
@@ -229,6 +244,21 @@ def test_bf16_gemv_full_size_sampled_rows(m, n, k, variant):
     check_gemv(got[:, rows], acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [4, 17])
+@pytest.mark.parametrize("n,k,silu", [(4112, 64, False), (4144, 32, False), (8256, 64, True)])
+def test_bf16_gemv_many_row_tiles(m, n, k, silu):
+    """More 16-row tiles than compute units, an odd number of them: the last
+    two-tile workgroup has one tile past the end."""
+    _say("bf16_gemv many tiles", m, n, k, silu)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + n + k)
+    got = run_bf16(d, silu=silu)
+    want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, 1.0, f"bf16 silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
 @pytest.mark.parametrize("m", [1, 3, 8, 32])
 def test_bf16_gemv_silu(m, gemv_path):
@@ -285,6 +315,42 @@ def test_moe_small_shapes(m, e, topk, h, inter, si):
     tok = synth.moe_tokens(m, h, e, topk, seed=400 + m)
     act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe M={m}")
+
+
+def test_moe_duplicate_experts_within_a_token():
+    """A token routed twice to one expert: both slots count (two act rows,
+    two weighted terms of the combine)."""
+    m, e, topk, h, inter, si = 5, 6, 4, 128, 128, 64
+    wts = synth.moe_weights(e, h, inter, si, seed=351)
+    tok = synth.moe_tokens(m, h, e, topk, seed=352)
+    ids = torch.tensor([[3, 3, 1, 5], [0, 0, 0, 0], [2, 4, 2, 4], [5, 1, 3, 3], [1, 2, 3, 4]], dtype=torch.int32)
+    tok["ids"] = ids
+    _say("moe duplicates", m, e, topk)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), "moe duplicates")
+
+
+def test_moe_most_pairs():
+    """32 tokens x 16 slots: the largest routing table, experts shared by
+    many tokens."""
+    m, e, topk, h, inter, si = 32, 40, 16, 128, 64, 128
+    wts = synth.moe_weights(e, h, inter, si, seed=361)
+    tok = synth.moe_tokens(m, h, e, topk, seed=362)
+    _say("moe most pairs", m, e, topk)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, [0, 1, 15, 30, 31], "moe most pairs")
+
+
+def test_moe_many_experts():
+    """More experts than the routing kernels' LDS table holds: the scan
+    fallback finds each expert's first pair."""
+    m, e, topk, h, inter, si = 3, 2100, 4, 64, 64, 64
+    wts = synth.moe_weights(e, h, inter, si, seed=371)
+    tok = synth.moe_tokens(m, h, e, topk, seed=372)
+    tok["ids"][1] = torch.tensor([2099, 7, 2099 - 64, 7], dtype=torch.int32)  # a repeat and high ids
+    _say("moe many experts", m, e, topk)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), "moe many experts")
 
 
 @pytest.fixture(scope="module")

@@ -1,4 +1,5 @@
-// The VALU "unit" used by the small-M dense GEMV and the MoE kernels.
+// The VALU "unit" of the small-M dense GEMV kernels (the row-set helpers
+// quad_rows / consecutive_rows also serve the MoE kernels).
 //
 // A unit is a set of R weight rows (4, or 8 = gate quad + up quad) that a
 // group of LPQ lanes reduces over the whole K extent.  K is cut into tiles:
