@@ -126,6 +126,48 @@ __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
 }
 
+// 16-byte buffer load straight into LDS: lane l's 16 bytes land at byte 16*l
+// of `dst`, a wave-uniform LDS address; out-of-range dwords are written as
+// zeros.  These loads count in vmcnt like any other, but the compiler does not
+// order later LDS reads after them: a reader waits with vm_wait<N>() (N = the
+// loads issued after the ones it needs), and a slot is refilled only after
+// lds_wait() has retired the reads of its previous contents.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void bload16_lds(rsrc_t r, void* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, static_cast<int>(off), 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// vm_wait<n>() for an n that is a constant once the caller is unrolled (the
+// switch folds away).
+__device__ __forceinline__ void vm_wait_n(int n) {
+  switch (n) {
+#define W4A16_VM_CASE(i) \
+  case i:                \
+    vm_wait<i>();        \
+    break;
+    W4A16_VM_CASE(0) W4A16_VM_CASE(1) W4A16_VM_CASE(2) W4A16_VM_CASE(3) W4A16_VM_CASE(4) W4A16_VM_CASE(5)
+    W4A16_VM_CASE(6) W4A16_VM_CASE(7) W4A16_VM_CASE(8) W4A16_VM_CASE(9) W4A16_VM_CASE(10) W4A16_VM_CASE(11)
+    W4A16_VM_CASE(12) W4A16_VM_CASE(13) W4A16_VM_CASE(14) W4A16_VM_CASE(15) W4A16_VM_CASE(16) W4A16_VM_CASE(17)
+    W4A16_VM_CASE(18) W4A16_VM_CASE(19) W4A16_VM_CASE(20) W4A16_VM_CASE(21) W4A16_VM_CASE(22) W4A16_VM_CASE(23)
+    W4A16_VM_CASE(24) W4A16_VM_CASE(25) W4A16_VM_CASE(26) W4A16_VM_CASE(27) W4A16_VM_CASE(28) W4A16_VM_CASE(29)
+    W4A16_VM_CASE(30) W4A16_VM_CASE(31) W4A16_VM_CASE(32) W4A16_VM_CASE(33) W4A16_VM_CASE(34) W4A16_VM_CASE(35)
+    W4A16_VM_CASE(36) W4A16_VM_CASE(37) W4A16_VM_CASE(38) W4A16_VM_CASE(39) W4A16_VM_CASE(40) W4A16_VM_CASE(41)
+    W4A16_VM_CASE(42) W4A16_VM_CASE(43) W4A16_VM_CASE(44) W4A16_VM_CASE(45) W4A16_VM_CASE(46) W4A16_VM_CASE(47)
+    W4A16_VM_CASE(48) W4A16_VM_CASE(49) W4A16_VM_CASE(50) W4A16_VM_CASE(51) W4A16_VM_CASE(52) W4A16_VM_CASE(53)
+    W4A16_VM_CASE(54) W4A16_VM_CASE(55) W4A16_VM_CASE(56) W4A16_VM_CASE(57) W4A16_VM_CASE(58) W4A16_VM_CASE(59)
+    W4A16_VM_CASE(60) W4A16_VM_CASE(61) W4A16_VM_CASE(62)
+#undef W4A16_VM_CASE
+    default:
+      vm_wait<0>();
+      break;
+  }
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -427,15 +427,24 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // (q = tile % 8): their scale words for a 64-k tile are 64 contiguous bytes.
 // BF16 tile rows are 16 consecutive rows.
 //
-// One workgroup per row tile (plus the matching up tile with silu_mul); its
-// kMfmaWaves waves split K into contiguous slices and meet in LDS at the end.  A
-// step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes feeding 4
-// MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights feeding 1
-// MFMA).  Each wave keeps D steps in flight in a ring: for every step the B
-// fragments (read straight from x) are issued before the weights, so the
-// in-order wait for a step's x never waits behind the HBM stream, and every
-// ring iteration issues the same loads (steps past the wave's share read
-// zeros through out-of-range offsets), which keeps the waits exact.
+// A workgroup takes RT row tiles (plus the matching up tiles with silu_mul);
+// its kMfmaWaves waves split K into contiguous slices and meet in LDS at the
+// end.  A step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes
+// feeding 4 MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights
+// feeding 1 MFMA).  Each wave keeps D steps in flight in a ring: while the
+// ring has later steps to fetch, every slot is refilled as soon as it is
+// consumed, so each wait is the same in-order count; the last round drains
+// the ring without refilling it.
+//
+// Activations are staged through the ring in LDS.  Every workgroup reads all
+// M*K*2 activation bytes, so at M >= 8 they are most of the bytes that reach
+// a compute unit.  Loaded straight into B fragments, a 1 KB load would touch
+// 16 token rows and 32 cache lines.  Here each 16-byte load goes straight
+// into LDS and covers whole token segments of one step (4 tokens x 256
+// bytes for NVFP4, 16 x 64 for BF16), and the fragments are then read with
+// ds_read_b128.  Chunk c of a token's segment sits at position c ^ swz(token),
+// so the 8 or 16 lanes that a fragment read serves in one LDS pass hit
+// distinct banks.
 constexpr int kMfmaWaves = 4;
 
 template <bool FP4>
@@ -444,17 +453,70 @@ __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
   else return tile * 16 + r;
 }
 
+// Ring position of activation chunk c (16 bytes) of token t (0..31) in its
+// token segment of CPT chunks.
+template <int CPT>
+__device__ __forceinline__ int xl_pos(int t, int c) {
+  if constexpr (CPT == 16) return c ^ (t & 15);
+  else return c ^ (((t >> 2) ^ (t >> 1)) & 3);
+}
+
+// Ring slot I of the staged activations, N chunks for all waves.  Each slot
+// is an LDS allocation of its own: the compiler then knows that a read of
+// one slot does not depend on the loads in flight into the others, and adds
+// no wait of its own for them.
+template <int I, int N>
+__device__ __forceinline__ u32x4* xl_slot() {
+  __shared__ u32x4 slot[N];
+  return slot;
+}
+
+template <int N>
+__device__ __forceinline__ u32x4* xl_slot(int d) {
+  static_assert(N > 0);
+  switch (d) {
+    case 0: return xl_slot<0, N>();
+    case 1: return xl_slot<1, N>();
+    case 2: return xl_slot<2, N>();
+    case 3: return xl_slot<3, N>();
+    case 4: return xl_slot<4, N>();
+    case 5: return xl_slot<5, N>();
+    case 6: return xl_slot<6, N>();
+    default: return xl_slot<7, N>();
+  }
+}
+
+// Steps in flight per wave (measured: deeper rings were slower), bounded by
+// vmcnt, which counts at most 63 outstanding loads.  A depth that divides
+// the steps of a wave wastes nothing in the last round; K = 4096 gives 8
+// NVFP4 steps and 32 BF16 steps per wave.
+template <bool FP4, int NT, int NA>
+constexpr int mfma_depth() {
+  const int per = FP4 ? 2 : 1;                   // loads per A operand and step
+  const int load_x = FP4 ? 4 * NT : NT;          // staging loads per step
+  int d = FP4 ? 4 : (NT == 1 ? 4 : 8);
+  while (d > 2 && NA * per + (d - 1) * (load_x + NA * per) > 62) --d;
+  return d;
+}
+
 template <bool FP4, int NT, bool SILU, int RT>
 __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams p) {
   constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
   constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
   constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
-  constexpr int D = FP4 ? 4 : (NT == 1 ? 16 : 8);  // steps in flight per wave
+  constexpr int D = mfma_depth<FP4, NT, NA>();  // steps in flight per wave
   constexpr int W = kMfmaWaves;
+  constexpr int CPT = KSTEP * 2 / 16;       // 16-byte activation chunks per token and step
+  constexpr int LX = NT * 16 * CPT / 64;    // staging loads per step
+  constexpr int PER = FP4 ? 2 : 1;          // weight-side loads per A operand and step
+  constexpr int L = LX + NA * PER;          // loads per step
+  // loads issued after a step's staging loads while it is the oldest in a full ring
+  constexpr int FULL_AFTER = NA * PER + (D - 1) * L;
   __shared__ f32x4 red[W - 1][NA][NT][64];
+  constexpr int SLOT = NT * 16 * CPT;        // ring chunks per wave and step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15;
   const int g = lane >> 4;
   const int64_t limit = SILU ? p.half : p.N;
@@ -467,6 +529,16 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
   const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   const float gs = FP4 ? *p.gs : 1.0f;
+
+  // Staging load i of a step: this lane fetches chunk skc[i] / 8 of token
+  // i * (64 / CPT) + lane / CPT into ring position lane % CPT of that token.
+  uint32_t sxo[LX], skc[LX];
+#pragma unroll
+  for (int i = 0; i < LX; ++i) {
+    const int t = i * (64 / CPT) + lane / CPT;
+    skc[i] = static_cast<uint32_t>(xl_pos<CPT>(t, lane % CPT)) * 8;  // the XOR is its own inverse
+    sxo[i] = t < p.M ? static_cast<uint32_t>(t) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
+  }
 
   for (int64_t tile = xcd_logical_block(); tile < p.units; tile += gridDim.x) {
     // A operand a: row tile tile*RT + a % RT, the up half for a >= RT
@@ -481,25 +553,16 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
         rv[RT + a] = rv[a];
       }
     }
-    // x offsets of this lane's B fragments: token 16n + r (bytes), zero past M
-    uint32_t xo[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int m = 16 * n + r;
-      xo[n] = m < p.M ? static_cast<uint32_t>(m) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
-    }
-    u32x4 xb[D][NJ][NT];
     u32x4 wb[D][NA];
     uint32_t sb[D][NA];
     auto issue = [&](int d, int64_t st) {
       const bool sv = st < nst;
       const uint32_t kb = static_cast<uint32_t>((st0 + st) * KSTEP);  // first k of the step
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint32_t k = kb + (FP4 ? g * 32 + 8 * j : g * 8);
-        const bool ok = sv && k < static_cast<uint32_t>(p.K);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) xb[d][j][n] = bload16(rx, ok ? xo[n] + k * 2 : kOutOfRange);
+      for (int i = 0; i < LX; ++i) {
+        const uint32_t k = kb + skc[i];
+        bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64,
+                    off_if(sv && k < static_cast<uint32_t>(p.K), sxo[i] + k * 2));
       }
       const uint32_t k = kb + (FP4 ? g * 32 : g * 8);
       const bool kv = sv && k < static_cast<uint32_t>(p.K);
@@ -525,34 +588,58 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[a][n] = f32x4{0, 0, 0, 0};
 
-    for (int64_t base = 0; base < nst; base += D) {
+    // Slot d of the ring holds step base + d.  `after` = loads issued after
+    // the slot's staging loads (a compile-time count once d is unrolled).
+    auto consume = [&](int d, int after) {
+      u32x4 xf[NJ][NT];
+      vm_wait_n(after);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int t = 16 * n + r;
+          xf[j][n] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, FP4 ? 4 * g + j : g)];
+        }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          bf16x8 av;
+          if constexpr (FP4) {
+            const uint32_t sw = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
+            const float scale = (j < 2) ? e4m3_to_f32<0>(sw) : e4m3_to_f32<1>(sw);
+            const uint32_t word = (j == 0) ? wb[d][a].x : (j == 1) ? wb[d][a].y : (j == 2) ? wb[d][a].z : wb[d][a].w;
+            uint32_t pr[4];
+            dequant_dword(word, scale, pr);
+            av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+          } else {
+            av = __builtin_bit_cast(bf16x8, wb[d][a]);
+          }
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xf[j][n]),
+                                                                acc[a][n], 0, 0, 0);
+        }
+      }
+    };
+
+    // Rounds that have steps after them: consume each slot, then refill it
+    // with the step D later (the ring stays full, so the wait is the same
+    // for every slot).
+    int64_t base = 0;
+    for (; base + D < nst; base += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        // consume slot d in place, then refill it with step base + d + D
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-          for (int a = 0; a < NA; ++a) {
-            bf16x8 av;
-            if constexpr (FP4) {
-              const uint32_t sw = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
-              const float scale = (j < 2) ? e4m3_to_f32<0>(sw) : e4m3_to_f32<1>(sw);
-              const uint32_t word = (j == 0) ? wb[d][a].x : (j == 1) ? wb[d][a].y : (j == 2) ? wb[d][a].z : wb[d][a].w;
-              uint32_t pr[4];
-              dequant_dword(word, scale, pr);
-              av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
-            } else {
-              av = __builtin_bit_cast(bf16x8, wb[d][a]);
-            }
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-              acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xb[d][j][n]),
-                                                                  acc[a][n], 0, 0, 0);
-          }
-        }
+        consume(d, FULL_AFTER);
+        lds_wait();  // the slot's fragment reads retire before it is refilled
         issue(d, base + d + D);
       }
     }
+    // The last round drains the ring without refilling it (no loads past the
+    // wave's share).  It runs even for a wave without steps: its waits retire
+    // every load into LDS before the slots are reused or the wave ends.
+#pragma unroll
+    for (int d = 0; d < D; ++d) consume(d, NA * PER + (D - 1 - d) * L);
 
     // The W K slices meet in LDS; wave 0 adds them in slice order and writes.
     if (wave > 0) {
