@@ -487,33 +487,41 @@ __device__ __forceinline__ u32x4* xl_slot(int d) {
 }
 
 // Steps in flight per wave (measured: deeper rings were slower), bounded by
-// vmcnt, which counts at most 63 outstanding loads.  A depth that divides
-// the steps of a wave wastes nothing in the last round; K = 4096 gives 8
-// NVFP4 steps and 32 BF16 steps per wave.
-template <bool FP4, int NT, int NA>
+// vmcnt, which counts at most 63 outstanding loads, and by the LDS ring
+// (128 KB per workgroup).  A depth that divides the steps of a wave wastes
+// nothing in the last round; K = 4096 gives 8 NVFP4 steps and 32 BF16 steps
+// per wave.
+template <bool FP4, int XT, int NA, int W>
 constexpr int mfma_depth() {
   const int per = FP4 ? 2 : 1;                   // loads per A operand and step
-  const int load_x = FP4 ? 4 * NT : NT;          // staging loads per step
-  int d = FP4 ? 4 : (NT == 1 ? 4 : 8);
-  while (d > 2 && NA * per + (d - 1) * (load_x + NA * per) > 62) --d;
+  const int cpt = FP4 ? 16 : 4;                  // 16-byte chunks per token and step
+  const int load_x = XT * cpt / 64;              // staging loads per step
+  int d = FP4 ? 4 : (XT <= 16 ? 4 : 8);
+  while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) --d;
   return d;
 }
 
-template <bool FP4, int NT, bool SILU, int RT>
+// XT: token rows staged per step (8, 16 or 32; 8 only for NVFP4, whose
+// step segment is 256 bytes per token).  With XT = 8 the fragment lanes of
+// tokens 8..15 read the rows of tokens 0..7 again: those MFMA columns are
+// never stored.
+template <bool FP4, int XT, bool SILU, int RT>
 __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams p) {
+  constexpr int NT = (XT + 15) / 16;        // token tiles (B operands)
   constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
   constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
   constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
-  constexpr int D = mfma_depth<FP4, NT, NA>();  // steps in flight per wave
+  constexpr int D = mfma_depth<FP4, XT, NA, kMfmaWaves>();  // steps in flight per wave
   constexpr int W = kMfmaWaves;
   constexpr int CPT = KSTEP * 2 / 16;       // 16-byte activation chunks per token and step
-  constexpr int LX = NT * 16 * CPT / 64;    // staging loads per step
+  constexpr int LX = XT * CPT / 64;         // staging loads per step
+  static_assert(XT * CPT % 64 == 0, "a staging load covers whole token segments");
   constexpr int PER = FP4 ? 2 : 1;          // weight-side loads per A operand and step
   constexpr int L = LX + NA * PER;          // loads per step
   // loads issued after a step's staging loads while it is the oldest in a full ring
   constexpr int FULL_AFTER = NA * PER + (D - 1) * L;
   __shared__ f32x4 red[W - 1][NA][NT][64];
-  constexpr int SLOT = NT * 16 * CPT;        // ring chunks per wave and step
+  constexpr int SLOT = XT * CPT;             // ring chunks per wave and step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -597,7 +605,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams 
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const int t = 16 * n + r;
+          const int t = (16 * n + r) & (XT - 1);
           xf[j][n] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, FP4 ? 4 * g + j : g)];
         }
 #pragma unroll
@@ -732,8 +740,10 @@ hipError_t launch_vchunk_c(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Largest M the NVFP4 GEMV sends to the VALU path by default.
-constexpr int64_t kValuMaxMFp4 = 4;
+// Largest M the NVFP4 GEMV sends to the VALU path by default.  The MFMA
+// path costs about the same for every M up to 8 (weight stream and dequant),
+// and from M = 3 it is the faster one.
+constexpr int64_t kValuMaxMFp4 = 2;
 
 // NVFP4 rows of at most kVchunkMaxK columns: 8-k chunks, at most 8 per lane
 // and 4 waves per unit.
@@ -779,18 +789,18 @@ hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
   }
 }
 
-template <bool FP4, int NT, bool SILU, int RT>
+template <bool FP4, int XT, bool SILU, int RT>
 hipError_t launch_mfma_rt(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   p.units = (tiles + RT - 1) / RT;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s, %d>", tf(FP4), NT, tf(SILU), RT);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s, %d>", tf(FP4), XT, tf(SILU), RT);
     return hipSuccess;
   }
   int64_t blocks = p.units;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((k_gemv_mfma<FP4, NT, SILU, RT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((k_gemv_mfma<FP4, XT, SILU, RT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kMfmaWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -815,12 +825,12 @@ int device_cu_count() {
 // round instead of leaving some units with twice the work of the others.
 int mfma_row_tiles(int64_t tiles) { return tiles > device_cu_count() ? 2 : 1; }
 
-template <bool FP4, int NT, bool SILU>
+template <bool FP4, int XT, bool SILU>
 hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
-  if (mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, NT, SILU, 2>(p, stream);
-  return launch_mfma_rt<FP4, NT, SILU, 1>(p, stream);
+  if (mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
+  return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
 template <bool FP4, bool SILU>
@@ -841,8 +851,9 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
     return launch_valu<FP4, 2, SILU>(p, lpq, stream);
   }
   p.tiles = p.K / 64;
-  if (p.M <= 16) return launch_mfma<FP4, 1, SILU>(p, stream);
-  return launch_mfma<FP4, 2, SILU>(p, stream);
+  if (FP4 && p.M <= 8) return launch_mfma<FP4, FP4 ? 8 : 16, SILU>(p, stream);
+  if (p.M <= 16) return launch_mfma<FP4, 16, SILU>(p, stream);
+  return launch_mfma<FP4, 32, SILU>(p, stream);
 }
 
 }  // namespace
