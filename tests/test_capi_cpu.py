@@ -140,12 +140,12 @@ def test_gemv_kernel_name_query(monkeypatch):
         assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_vchunk<{m}, false,")
         assert gemv_kernel_name(m, 28672, 4096, silu_mul=True).startswith(f"k_gemv_vchunk<{m}, true,")
     # the MFMA kernels are named by the token rows they stage per step
-    for m, xt in ((3, 8), (4, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32)):
+    for m, xt in ((3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32)):
         assert gemv_kernel_name(m, 6144, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 16, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")
-    assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 8, false,")
+    assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "valu")
     assert gemv_kernel_name(4, 4096, 4096).startswith("k_gemv_vchunk<4, false,")
     for bad in (dict(m=0, n=16, k=64), dict(m=33, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):

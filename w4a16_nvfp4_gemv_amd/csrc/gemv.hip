@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // BF16 tile rows are 16 consecutive rows.
 //
 // A workgroup takes RT row tiles (plus the matching up tiles with silu_mul);
-// its kMfmaWaves waves split K into contiguous slices and meet in LDS at the
+// its mfma_waves(XT) waves split K into contiguous slices and meet in LDS at the
 // end.  A step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes
 // feeding 4 MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights
 // feeding 1 MFMA).  Each wave keeps D steps in flight in a ring: while the
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // ds_read_b128.  Chunk c of a token's segment sits at position c ^ swz(token),
 // so the 8 or 16 lanes that a fragment read serves in one LDS pass hit
 // distinct banks.
-constexpr int kMfmaWaves = 4;
+constexpr int mfma_waves(int XT) { return XT > 0 ? 4 : 4; }
 
 template <bool FP4>
 __device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
@@ -497,22 +497,22 @@ constexpr int mfma_depth() {
   const int cpt = FP4 ? 16 : 4;                  // 16-byte chunks per token and step
   const int load_x = XT * cpt / 64;              // staging loads per step
   int d = FP4 ? 4 : (XT <= 16 ? 4 : 8);
-  while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) --d;
+  while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) d /= 2;
   return d;
 }
 
-// XT: token rows staged per step (8, 16 or 32; 8 only for NVFP4, whose
-// step segment is 256 bytes per token).  With XT = 8 the fragment lanes of
-// tokens 8..15 read the rows of tokens 0..7 again: those MFMA columns are
-// never stored.
+// XT: token rows staged per step (4, 8, 16 or 32; 4 and 8 only for NVFP4,
+// whose step segment is 256 bytes per token).  With XT < 16 the fragment
+// lanes of tokens XT..15 read the rows of tokens 0..XT-1 again: those MFMA
+// columns are never stored.
 template <bool FP4, int XT, bool SILU, int RT>
-__global__ __launch_bounds__(kMfmaWaves * 64) void k_gemv_mfma(const GemvParams p) {
+__global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvParams p) {
   constexpr int NT = (XT + 15) / 16;        // token tiles (B operands)
   constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
   constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
   constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
-  constexpr int D = mfma_depth<FP4, XT, NA, kMfmaWaves>();  // steps in flight per wave
-  constexpr int W = kMfmaWaves;
+  constexpr int W = mfma_waves(XT);
+  constexpr int D = mfma_depth<FP4, XT, NA, W>();  // steps in flight per wave
   constexpr int CPT = KSTEP * 2 / 16;       // 16-byte activation chunks per token and step
   constexpr int LX = XT * CPT / 64;         // staging loads per step
   static_assert(XT * CPT % 64 == 0, "a staging load covers whole token segments");
@@ -801,7 +801,7 @@ hipError_t launch_mfma_rt(GemvParams p, hipStream_t stream) {
   int64_t blocks = p.units;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL((k_gemv_mfma<FP4, XT, SILU, RT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kMfmaWaves * 64), 0, stream, p);
+                     dim3(mfma_waves(XT) * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -829,7 +829,8 @@ template <bool FP4, int XT, bool SILU>
 hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
-  if (mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
+  // (one tile per workgroup at XT = 4: measured faster there)
+  if (XT > 4 && mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
   return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
@@ -851,6 +852,7 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
     return launch_valu<FP4, 2, SILU>(p, lpq, stream);
   }
   p.tiles = p.K / 64;
+  if (FP4 && p.M <= 4) return launch_mfma<FP4, FP4 ? 4 : 16, SILU>(p, stream);
   if (FP4 && p.M <= 8) return launch_mfma<FP4, FP4 ? 8 : 16, SILU>(p, stream);
   if (p.M <= 16) return launch_mfma<FP4, 16, SILU>(p, stream);
   return launch_mfma<FP4, 32, SILU>(p, stream);
