@@ -305,8 +305,10 @@ def moe_check(wts, tok, act, sact, out, tokens, what):
 
 @pytest.mark.parametrize("m,e,topk,h,inter,si", [
     (1, 4, 2, 256, 128, 128),
+    (2, 6, 3, 192, 64, 128),      # two tokens: the VALU forms with token pairs
     (3, 6, 3, 128, 192, 64),      # I not a multiple of 128: unaligned up quad
     (5, 8, 4, 512, 256, 320),
+    (16, 12, 4, 320, 448, 192),   # H, I, SI not multiples of 128; shared expert in two token groups
     (32, 16, 8, 256, 128, 128),
 ])
 def test_moe_small_shapes(m, e, topk, h, inter, si):

@@ -166,6 +166,26 @@ __device__ __forceinline__ void vm_wait_n(int n) {
       break;
   }
 }
+// LDS accesses written as their own instructions, so that the compiler, which
+// cannot tell LDS tables apart from ring slots that loads are still writing,
+// adds no vmcnt wait in front of them.  Only for LDS data that those loads do
+// not write.  lds_read_u32 retires before it returns; stores and adds retire
+// with the next lds_wait(), which the caller issues before any barrier that
+// publishes them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint32_t*)(p)));
+}
+__device__ __forceinline__ uint32_t lds_read_u32(const void* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)));
+  return v;
+}
+__device__ __forceinline__ void lds_store_f32(float* p, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v));
+}
+__device__ __forceinline__ void lds_add_f32(float* p, float v) {
+  asm volatile("ds_add_f32 %0, %1" ::"v"(lds_addr(p)), "v"(v));
+}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

@@ -22,6 +22,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_core.hpp"
 #include "unit_core.hpp"
 
 namespace w4a16 {
@@ -445,46 +446,7 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // ds_read_b128.  Chunk c of a token's segment sits at position c ^ swz(token),
 // so the 8 or 16 lanes that a fragment read serves in one LDS pass hit
 // distinct banks.
-constexpr int mfma_waves(int XT) { return XT > 0 ? 4 : 4; }
-
-template <bool FP4>
-__device__ __forceinline__ int64_t mfma_row(int64_t tile, int r) {
-  if constexpr (FP4) return (tile >> 3) * 128 + (tile & 7) * 4 + (r & 3) + 32 * (r >> 2);
-  else return tile * 16 + r;
-}
-
-// Ring position of activation chunk c (16 bytes) of token t (0..31) in its
-// token segment of CPT chunks.
-template <int CPT>
-__device__ __forceinline__ int xl_pos(int t, int c) {
-  if constexpr (CPT == 16) return c ^ (t & 15);
-  else return c ^ (((t >> 2) ^ (t >> 1)) & 3);
-}
-
-// Ring slot I of the staged activations, N chunks for all waves.  Each slot
-// is an LDS allocation of its own: the compiler then knows that a read of
-// one slot does not depend on the loads in flight into the others, and adds
-// no wait of its own for them.
-template <int I, int N>
-__device__ __forceinline__ u32x4* xl_slot() {
-  __shared__ u32x4 slot[N];
-  return slot;
-}
-
-template <int N>
-__device__ __forceinline__ u32x4* xl_slot(int d) {
-  static_assert(N > 0);
-  switch (d) {
-    case 0: return xl_slot<0, N>();
-    case 1: return xl_slot<1, N>();
-    case 2: return xl_slot<2, N>();
-    case 3: return xl_slot<3, N>();
-    case 4: return xl_slot<4, N>();
-    case 5: return xl_slot<5, N>();
-    case 6: return xl_slot<6, N>();
-    default: return xl_slot<7, N>();
-  }
-}
+constexpr int mfma_waves(int /*XT*/) { return 4; }
 
 // Steps in flight per wave (measured: deeper rings were slower), bounded by
 // vmcnt, which counts at most 63 outstanding loads, and by the LDS ring
@@ -614,19 +576,13 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
         for (int a = 0; a < NA; ++a) {
           bf16x8 av;
           if constexpr (FP4) {
-            const uint32_t sw = sb[d][a] >> (16 * (g & 1));  // this lane's two scale bytes
-            const float scale = (j < 2) ? e4m3_to_f32<0>(sw) : e4m3_to_f32<1>(sw);
-            const uint32_t word = (j == 0) ? wb[d][a].x : (j == 1) ? wb[d][a].y : (j == 2) ? wb[d][a].z : wb[d][a].w;
-            uint32_t pr[4];
-            dequant_dword(word, scale, pr);
-            av = __builtin_bit_cast(bf16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+            av = fp4_a_fragment(wb[d][a], sb[d][a], g, j);
           } else {
             av = __builtin_bit_cast(bf16x8, wb[d][a]);
           }
 #pragma unroll
           for (int n = 0; n < NT; ++n)
-            acc[a][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, xf[j][n]),
-                                                                acc[a][n], 0, 0, 0);
+            acc[a][n] = mfma_16x16x32(av, xf[j][n], acc[a][n]);
         }
       }
     };

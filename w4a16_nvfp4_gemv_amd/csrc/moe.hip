@@ -8,30 +8,33 @@
 // order.  No host synchronization and no workspace are needed, and the order
 // of every floating-point sum depends on ids alone.
 //
-// gate_up.  One workgroup per gate quad of the routed experts' I rows and
-// per gate quad of the shared expert's SI rows.  A routed workgroup walks the
-// slots: for each, its four waves split the hidden size H of the expert's
-// gate and up quads (chunk-interleaved loads, chunk_core.hpp), meet in LDS,
-// and the results of the slot's tokens are kept in LDS; they are stored once
-// the walk is over.
-//   routed: act[p][i] = bf16(silu(g) * u),  g, u = FP32 sum * alpha[e]
-//   shared: sact[t][i] = bf16(silu(bf16(g)) * bf16(u)),  g, u = FP32 sum * gssh
+//   gate_up routed: act[p][i] = bf16(silu(g) * u),  g, u = FP32 sum * alpha[e]
+//   gate_up shared: sact[t][i] = bf16(silu(bf16(g)) * bf16(u)),  g, u = FP32 sum * gssh
+//   down_combine:   y = bf16(FP32 sum * alpha2[e]) per pair,
+//                   out = bf16(bf16(sum of tw * y) + y_shared)
 //
-// down_combine.  One workgroup per quad of the H output rows.  Its waves take
-// the slots round robin (slot D being the shared expert); for every token of
-// a slot the wave forms y = bf16(FP32 sum * alpha2[e]) and adds tw * y to its
-// own FP32 partial of that token in LDS.  The four partials are added in wave
-// order, then out = bf16(bf16(sum) + y_shared).
+// Two forms of each kernel:
 //
-// Both kernels stream their jobs (slot, group of tokens, K block) through a
-// two-slot ring of registers: a slot is consumed, then refilled in place with
-// the job two ahead, so one job's loads are in flight while the other is
-// computed.  No global store and no other vector load happens inside the
-// ring: vmcnt waits are in order, and a store or a late load among the loads
-// in flight would make every wait drain the ring.
+// VALU forms (M <= 2).  Chunk-interleaved loads and per-token dot products
+// (chunk_core.hpp).  gate_up walks persistent items (slot, quad of gate rows
+// and the matching up rows) with four waves splitting H and meeting in LDS;
+// down_combine gives a workgroup a quad of H rows, its waves take the slots
+// round robin and stream their jobs (slot, token group, K block) through a
+// two-slot ring of registers.
+//
+// MFMA forms (M >= 3).  The swap-AB MFMA building blocks of the dense GEMV
+// (mfma_core.hpp) with each slot's tokens gathered by the loads that stage
+// activations in LDS; the dequant then costs the same for any number of
+// tokens.  Each wave streams whole work units through one LDS ring (see the
+// section below).
+//
+// Inside every ring the loads are counted: no other vector memory access may
+// fall between them, and LDS tables are read with lds_read_u32 so that the
+// compiler adds no wait for the loads still writing ring slots.
 #include "chunk_core.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_core.hpp"
 #include "unit_core.hpp"
 
 namespace w4a16 {
@@ -52,6 +55,19 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  return static_cast<const uint8_t*>(uniform_ptr(static_cast<const void*>(p)));
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  return static_cast<int64_t>(reinterpret_cast<uint64_t>(uniform_ptr(reinterpret_cast<const void*>(v))));
+}
+// c ? a : b on values: a conditional between two named variables is an
+// lvalue, which the compiler may turn into a load from a chosen address and
+// so keep those variables in scratch memory.
+template <typename T>
+__device__ __forceinline__ T pick(bool c, T a, T b) {
+  return c ? a : b;
 }
 __device__ __forceinline__ rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
   return make_rsrc(uniform_ptr(base), __builtin_amdgcn_readfirstlane(bytes));
@@ -465,11 +481,426 @@ __global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p)
   }
 }
 
+// ------------------------------------------------------------------ MFMA forms
+// For M >= 2 both kernels use the swap-AB MFMA building blocks of the dense
+// GEMV (mfma_core.hpp): 16 weight rows are the A operand, up to XT tokens of
+// one slot the B operand, staged through a per-wave LDS ring by loads that
+// gather the slot's rows.  The dequant costs the same for any number of
+// tokens, where the VALU forms pay one dot product per token.
+//
+// Each wave owns a stream of jobs (work unit, group of XT tokens, 128-k
+// step) and runs the whole K of a unit itself, so nothing is reduced across
+// waves.  One ring of kMoeRing steps runs through all of a wave's jobs: a
+// slot is consumed, its LDS reads retired, and it is refilled with the job
+// kMoeRing ahead, so every wait counts the same loads; the last round drains
+// the ring without refilling it.  A job's results are written by the wave
+// that consumed its last step.
+constexpr int kMoeRing = 4;
+constexpr int kMoeDownRing = 4;
+constexpr int kMoeDownWaves = 12;
+constexpr int kMoeGateUpWaves = 4;
+
+// The job the wave issues next, and what a ring slot remembers of the job it
+// holds.  All fields are wave-uniform.
+struct MoeJob {
+  int unit;      // work unit (kernel-specific), < 0 once the stream is over
+  int slot;      // routing slot (== D: the shared expert)
+  int tile;      // 16-row tile
+  int cnt;       // tokens (pairs) of the slot
+  int first;     // offset of the slot's pairs in the routing order
+  int g0;        // first token of the group
+  int step;      // 128-k step within the unit
+  int nsteps;    // steps of the unit
+  float scale;   // alpha of the expert (or the shared global scale)
+  int expert;    // expert of the slot (0 for the shared expert)
+};
+
+// Job arithmetic shared by both kernels: next step, next group, next unit.
+template <int XT>
+__device__ __forceinline__ bool moe_job_next(MoeJob& j) {
+  if (++j.step < j.nsteps) return false;
+  j.step = 0;
+  j.g0 += XT;
+  return j.g0 >= j.cnt;  // the unit is done: the caller moves to its next one
+}
+
+// gate_up.  Work unit u = (slot, 16-row tile of its gate rows): the A
+// operands are the gate tile and the matching up tile (rows + half); units
+// u, u + (all waves), ... belong to one wave.
+//   routed: act[p][i] = bf16(silu(g) * u),  g, u = FP32 sum * alpha[e]
+//   shared: sact[t][i] = bf16(silu(bf16(g)) * bf16(u)),  g, u = FP32 sum * gssh
+template <int XT>
+__global__ __launch_bounds__(kMoeGateUpWaves * 64) void k_moe_gate_up_mfma(const MoeGateUpParams p) {
+  constexpr int W = kMoeGateUpWaves, D = kMoeRing, NA = 2, CPT = 16, LX = XT * CPT / 64, PER = 2;
+  constexpr int L = LX + NA * PER;              // loads per step
+  constexpr int FULL_AFTER = NA * PER + (D - 1) * L;
+  constexpr int SLOT = XT * CPT;                // ring chunks per wave and step
+  static_assert(XT * CPT % 64 == 0 && XT <= 16, "one token tile, whole token segments");
+  static_assert(FULL_AFTER < 63, "vmcnt");
+  __shared__ MoeRouting rt;
+  __shared__ float slot_scale[kMoeMaxPairs + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int P = p.M * p.topk;
+  build_routing(rt, p.ids, nullptr, P, p.E);
+  const int Ds = uniform(rt.D);
+  // every slot's scale, read before the ring (a load inside it would be a
+  // vector load: the kernel's own stores may alias alpha for all the
+  // compiler knows)
+  for (int s = tid; s <= Ds; s += blockDim.x) slot_scale[s] = s < Ds ? p.alpha[rt.expert[s]] : *p.gssh;
+  __syncthreads();
+  const int tiles_r = (p.I + 127) / 128 * 8;
+  const int tiles_s = (p.SI + 127) / 128 * 8;
+  // the shared expert's units are (tile, group of XT tokens), so that its
+  // M tokens spread over as many waves as a routed expert's few
+  const int groups_s = (p.M + XT - 1) / XT;
+  const int units = Ds * tiles_r + tiles_s * groups_s;
+  const int nsteps = (p.H + 127) / 128;
+  const uint32_t row_bytes = static_cast<uint32_t>(p.H) / 2;
+  const uint32_t tiles64 = static_cast<uint32_t>(p.H) / 64;
+  const rsrc_t rx = make_rsrc(p.x, static_cast<uint32_t>(p.M) * p.H * 2);
+  const int stride = gridDim.x * W;
+
+  // chunk of the lane's staging loads (its ring position is lane % CPT)
+  uint32_t skc[LX];
+#pragma unroll
+  for (int i = 0; i < LX; ++i) skc[i] = static_cast<uint32_t>(xl_pos<CPT>(i * (64 / CPT) + lane / CPT, lane % CPT)) * 8;
+
+  // the issue cursor and the per-lane state of its (unit, group)
+  MoeJob cur;
+  int64_t rows[NA];
+  bool rv[NA];
+  uint32_t sxo[LX];
+  rsrc_t rw = make_rsrc(p.w1, 0), rs = make_rsrc(p.w1s, 0);
+  auto load_unit = [&](int u) {
+    cur.unit = u < units ? u : -1;
+    cur.g0 = 0;
+    cur.step = 0;
+    cur.nsteps = nsteps;
+    if (cur.unit < 0) return;
+    const bool shared = u >= Ds * tiles_r;
+    const int us = u - Ds * tiles_r;  // shared unit: tile us % tiles_s, group us / tiles_s
+    cur.slot = shared ? Ds : u / tiles_r;
+    cur.tile = shared ? us % tiles_s : u - cur.slot * tiles_r;
+    const int e = shared ? 0 : uniform(static_cast<int>(lds_read_u32(&rt.expert[cur.slot])));
+    if (shared) cur.g0 = us / tiles_s * XT;
+    cur.cnt = shared ? (cur.g0 + XT < p.M ? cur.g0 + XT : p.M)
+                     : uniform(static_cast<int>(lds_read_u32(&rt.count[cur.slot])));
+    cur.first = shared ? 0 : uniform(static_cast<int>(lds_read_u32(&rt.start[cur.slot])));
+    cur.scale = __builtin_bit_cast(float, uniform(static_cast<int>(lds_read_u32(&slot_scale[cur.slot]))));
+    const int half = shared ? p.SI : p.I;
+    rw = uniform_rsrc(shared ? p.wsh : p.w1 + e * p.w1_expert_bytes,
+                      static_cast<uint32_t>(shared ? p.wsh_bytes : p.w1_expert_bytes));
+    rs = uniform_rsrc(shared ? p.ssh : p.w1s + e * p.s1_expert_bytes,
+                      static_cast<uint32_t>(shared ? p.ssh_bytes : p.s1_expert_bytes));
+    rows[0] = mfma_row<true>(cur.tile, r);
+    rv[0] = rows[0] < half;
+    rows[1] = rows[0] + half;
+    rv[1] = rv[0];
+  };
+  auto load_group = [&]() {
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+      const int idx = cur.g0 + i * (64 / CPT) + lane / CPT;
+      const bool ok = cur.unit >= 0 && idx < cur.cnt;
+      const bool shared = cur.slot == Ds;
+      const int t = shared ? idx : static_cast<int>(lds_read_u32(&rt.order[cur.first + (ok ? idx : 0)])) / p.topk;
+      sxo[i] = off_if(ok, static_cast<uint32_t>(t) * p.H * 2);
+    }
+  };
+
+  u32x4 wb[D][NA];
+  uint32_t sb[D][NA];
+  MoeJob held[D];
+  auto issue = [&](int d) {
+    const bool valid = cur.unit >= 0;
+    const uint32_t kb = static_cast<uint32_t>(cur.step) * 128;
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+      const uint32_t k = kb + skc[i];
+      bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64,
+                  off_if(valid && k < static_cast<uint32_t>(p.H), sxo[i] + k * 2));
+    }
+    const uint32_t k = kb + g * 32;
+    const bool kv = valid && k < static_cast<uint32_t>(p.H);
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const bool ok = rv[a] && kv;
+      sb[d][a] = bload4(rs, off_if(ok, static_cast<uint32_t>(scale_word_offset(rows[a], k / 64, tiles64))));
+      wb[d][a] = bload16_nt(rw, off_if(ok, static_cast<uint32_t>(rows[a]) * row_bytes + k / 2));
+    }
+    held[d] = cur;
+    __builtin_amdgcn_sched_barrier(0);
+    if (valid && moe_job_next<XT>(cur)) {
+      load_unit(cur.unit + stride);
+      load_group();
+    } else if (valid && cur.step == 0) {
+      load_group();
+    }
+  };
+
+  f32x4 acc[NA];
+  auto finish = [&](const MoeJob& j) {
+    const bool shared = j.slot == Ds;
+    const int half = shared ? p.SI : p.I;
+    const int idx = j.g0 + (lane & 15);
+    if ((lane & 15) < XT && idx < j.cnt) {
+      const int pair = shared ? 0 : static_cast<int>(lds_read_u32(&rt.order[j.first + idx]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = mfma_row<true>(j.tile, 4 * (lane >> 4) + i);
+        if (row >= half) continue;
+        float gv = acc[0][i] * j.scale, uv = acc[1][i] * j.scale;
+        if (shared) {
+          gv = bf16_bits_to_f32(f32_to_bf16_bits(gv));
+          uv = bf16_bits_to_f32(f32_to_bf16_bits(uv));
+          p.sact[static_cast<int64_t>(idx) * p.SI + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+        } else {
+          p.act[static_cast<int64_t>(pair) * p.I + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+        }
+      }
+    }
+  };
+  auto consume = [&](int d, int after) {
+    vm_wait_n(after);
+    u32x4 xf[4];
+    const int t = r & (XT - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, 4 * g + j)];
+    if (held[d].step == 0) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[a] = f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int a = 0; a < NA; ++a) acc[a] = mfma_16x16x32(fp4_a_fragment(wb[d][a], sb[d][a], g, j), xf[j], acc[a]);
+    if (held[d].unit >= 0 && held[d].step == held[d].nsteps - 1) finish(held[d]);
+  };
+
+  load_unit(blockIdx.x * W + wave);
+  load_group();
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
+  while (cur.unit >= 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      consume(d, FULL_AFTER);
+      lds_wait();  // the slot's fragment reads retire before it is refilled
+      issue(d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) consume(d, NA * PER + (D - 1 - d) * L);
+}
+
+// down_combine.  A workgroup per 16-row tile of H; its waves take the slots
+// round robin (slot D being the shared expert) and run each slot's K (I or
+// SI) through their ring, so a slot's job stream is one unit per token
+// group.  For every pair the wave forms y = bf16(FP32 sum * alpha2[e]) and
+// adds tw * y to its own FP32 partial of the pair's token in LDS, one token
+// column at a time (two pairs of a group may share a token); the shared
+// expert's y goes to its own LDS rows.  The four partials are added in wave
+// order, then out = bf16(bf16(sum) + y_shared).
+template <int XT>
+__global__ __launch_bounds__(kMoeDownWaves * 64) void k_moe_down_mfma(const MoeDownParams p) {
+  constexpr int W = kMoeDownWaves, D = kMoeDownRing, NA = 1, CPT = 16, LX = XT * CPT / 64, PER = 2;
+  constexpr int L = LX + NA * PER;
+  constexpr int FULL_AFTER = NA * PER + (D - 1) * L;
+  constexpr int SLOT = XT * CPT;
+  static_assert(XT * CPT % 64 == 0 && XT <= 16, "one token tile, whole token segments");
+  static_assert(FULL_AFTER < 63, "vmcnt");
+  __shared__ MoeRouting rt;
+  __shared__ float part[W][kMoeMaxTokens][16];
+  __shared__ float ysh[kMoeMaxTokens][16];
+  __shared__ float slot_scale[kMoeMaxPairs + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int P = p.M * p.topk;
+  build_routing(rt, p.ids, p.tw, P, p.E);
+  const int Ds = uniform(rt.D);
+  for (int s = tid; s <= Ds; s += blockDim.x) slot_scale[s] = s < Ds ? p.alpha2[rt.expert[s]] : *p.gssd;
+  __syncthreads();
+  const int tiles = (p.H + 127) / 128 * 8;
+  // Fields chosen per slot, read once into registers.  A choice between two
+  // fields of the parameter block would otherwise become one load from a
+  // chosen address, i.e. a copy of the block in scratch memory.
+  const uint32_t k_routed = static_cast<uint32_t>(uniform(p.I)), k_shared = static_cast<uint32_t>(uniform(p.SI));
+  const uint32_t act_bytes = static_cast<uint32_t>(P) * k_routed * 2;
+  const uint32_t sact_bytes = static_cast<uint32_t>(p.M) * k_shared * 2;
+  const int groups_s = (p.M + XT - 1) / XT;
+  const uint8_t* const w2 = uniform_ptr(p.w2);
+  const uint8_t* const w2s = uniform_ptr(p.w2s);
+  const uint8_t* const wsd = uniform_ptr(p.wsd);
+  const uint8_t* const ssd = uniform_ptr(p.ssd);
+  const void* const act = uniform_ptr(p.act);
+  const void* const sact = uniform_ptr(p.sact);
+  const int64_t w2_expert_bytes = uniform_i64(p.w2_expert_bytes), s2_expert_bytes = uniform_i64(p.s2_expert_bytes);
+  const uint32_t wsd_bytes = static_cast<uint32_t>(uniform(static_cast<int>(p.wsd_bytes)));
+  const uint32_t ssd_bytes = static_cast<uint32_t>(uniform(static_cast<int>(p.ssd_bytes)));
+
+  uint32_t skc[LX];
+#pragma unroll
+  for (int i = 0; i < LX; ++i) skc[i] = static_cast<uint32_t>(xl_pos<CPT>(i * (64 / CPT) + lane / CPT, lane % CPT)) * 8;
+
+  for (int tile = xcd_logical_block(); tile < tiles; tile += gridDim.x) {
+    for (int i = tid; i < W * kMoeMaxTokens * 16; i += blockDim.x) (&part[0][0][0])[i] = 0.0f;
+    for (int i = tid; i < kMoeMaxTokens * 16; i += blockDim.x) (&ysh[0][0])[i] = 0.0f;
+    __syncthreads();
+
+    MoeJob cur;
+    const int64_t row = mfma_row<true>(tile, r);
+    const bool rvalid = row < p.H;
+    uint32_t sxo[LX];
+    // Slots Ds .. Ds + groups_s - 1 are the shared expert's groups of XT
+    // tokens (cur.slot is then Ds), so that its M tokens spread over waves.
+    auto load_unit = [&](int s) {
+      cur.unit = s < Ds + groups_s ? s : -1;
+      cur.tile = tile;
+      cur.g0 = 0;
+      cur.step = 0;
+      if (cur.unit < 0) return;
+      const bool shared = s >= Ds;
+      cur.slot = shared ? Ds : s;
+      if (shared) cur.g0 = (s - Ds) * XT;
+      cur.expert = shared ? 0 : uniform(static_cast<int>(lds_read_u32(&rt.expert[s])));
+      cur.cnt = shared ? (cur.g0 + XT < p.M ? cur.g0 + XT : p.M)
+                       : uniform(static_cast<int>(lds_read_u32(&rt.count[s])));
+      cur.first = shared ? 0 : uniform(static_cast<int>(lds_read_u32(&rt.start[s])));
+      cur.scale = __builtin_bit_cast(float, uniform(static_cast<int>(lds_read_u32(&slot_scale[cur.slot]))));
+      cur.nsteps = static_cast<int>((pick(shared, k_shared, k_routed) + 127) / 128);
+    };
+    auto load_group = [&]() {
+      const bool shared = cur.slot == Ds;
+      const uint32_t kdim = pick(shared, k_shared, k_routed);
+#pragma unroll
+      for (int i = 0; i < LX; ++i) {
+        const int idx = cur.g0 + i * (64 / CPT) + lane / CPT;
+        const bool ok = cur.unit >= 0 && idx < cur.cnt;
+        const int xr = shared ? idx : static_cast<int>(lds_read_u32(&rt.order[cur.first + (ok ? idx : 0)]));  // token (shared) or pair row
+        sxo[i] = off_if(ok, static_cast<uint32_t>(xr) * kdim * 2);
+      }
+    };
+
+    u32x4 wb[D];
+    uint32_t sb[D];
+    MoeJob held[D];
+    auto issue = [&](int d) {
+      const bool valid = cur.unit >= 0;
+      const bool shared = cur.slot == Ds;
+      const uint32_t kdim = pick(shared, k_shared, k_routed);
+      const int64_t e = cur.expert;
+      const rsrc_t rw = uniform_rsrc(pick(shared, wsd, w2 + e * w2_expert_bytes),
+                                     pick(shared, wsd_bytes, static_cast<uint32_t>(w2_expert_bytes)));
+      const rsrc_t rs = uniform_rsrc(pick(shared, ssd, w2s + e * s2_expert_bytes),
+                                     pick(shared, ssd_bytes, static_cast<uint32_t>(s2_expert_bytes)));
+      const rsrc_t rx = uniform_rsrc(pick(shared, sact, act), pick(shared, sact_bytes, act_bytes));
+      const uint32_t kb = static_cast<uint32_t>(cur.step) * 128;
+#pragma unroll
+      for (int i = 0; i < LX; ++i) {
+        const uint32_t k = kb + skc[i];
+        bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64, off_if(valid && k < kdim, sxo[i] + k * 2));
+      }
+      const uint32_t k = kb + g * 32;
+      const bool ok = valid && rvalid && k < kdim;
+      sb[d] = bload4(rs, off_if(ok, static_cast<uint32_t>(scale_word_offset(row, k / 64, kdim / 64))));
+      wb[d] = bload16_nt(rw, off_if(ok, static_cast<uint32_t>(row) * (kdim / 2) + k / 2));
+      held[d] = cur;
+      __builtin_amdgcn_sched_barrier(0);
+      if (valid && moe_job_next<XT>(cur)) {
+        load_unit(cur.unit + W);
+        load_group();
+      } else if (valid && cur.step == 0) {
+        load_group();
+      }
+    };
+
+    f32x4 acc;
+    auto finish = [&](const MoeJob& j) {
+      const bool shared = j.slot == Ds;
+      const int c = lane & 15;
+      const int idx = j.g0 + c;
+      const bool has = c < XT && idx < j.cnt;
+      const int pair = has && !shared ? static_cast<int>(lds_read_u32(&rt.order[j.first + idx])) : 0;
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i] * j.scale));
+      if (shared) {
+        if (has) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lds_store_f32(&ysh[idx][4 * (lane >> 4) + i], y[i]);
+        }
+        return;
+      }
+      const float w = has ? __builtin_bit_cast(float, lds_read_u32(&rt.tw[pair])) : 0.0f;
+      const int tok = pair / p.topk;
+      // one token column at a time: two pairs of one group may share a token
+      for (int cc = 0; cc < XT; ++cc) {
+        if (has && c == cc) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lds_add_f32(&part[wave][tok][4 * (lane >> 4) + i], w * y[i]);
+        }
+      }
+    };
+    auto consume = [&](int d, int after) {
+      vm_wait_n(after);
+      u32x4 xf[4];
+      const int t = r & (XT - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[j] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, 4 * g + j)];
+      if (held[d].step == 0) acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma_16x16x32(fp4_a_fragment(wb[d], sb[d], g, j), xf[j], acc);
+      if (held[d].unit >= 0 && held[d].step == held[d].nsteps - 1) finish(held[d]);
+    };
+
+    load_unit(wave);
+    load_group();
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+    while (cur.unit >= 0) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        consume(d, FULL_AFTER);
+        lds_wait();
+        issue(d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) consume(d, NA * PER + (D - 1 - d) * L);
+    lds_wait();  // the partial and shared-expert updates above are not visible to the compiler
+    __syncthreads();
+    for (int i = tid; i < p.M * 16; i += blockDim.x) {
+      const int t = i >> 4, rr = i & 15;
+      const int64_t orow = mfma_row<true>(tile, rr);
+      if (orow < p.H) {
+        float s = part[0][t][rr];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s += part[w][t][rr];  // wave order
+        const float sr = bf16_bits_to_f32(f32_to_bf16_bits(s));
+        p.out[static_cast<int64_t>(t) * p.H + orow] = f32_to_bf16_bits(sr + ysh[t][rr]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ launch
 namespace {
 
 // Persistent gate_up workgroups: about five resident per CU.
 constexpr int64_t kMoeGateUpGrid = 1280;
+// Persistent MFMA gate_up workgroups: two per CU.
+constexpr int64_t kMoeMfmaGrid = 512;
+
+// The MFMA forms from three tokens up; one or two tokens keep the VALU
+// forms, whose per-token dot products then cost no more than the MFMA path's
+// dequant (measured on the 128-expert decode block).
+bool moe_use_mfma(int M) { return M >= 3; }
 
 template <int MT>
 hipError_t launch_gate_up_mt(const MoeGateUpParams& p, int c, hipStream_t stream) {
@@ -508,15 +939,31 @@ int chunks_per_lane(int64_t k, int64_t lanes, int cmax) {
 }  // namespace
 
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
-  const int c = chunks_per_lane(p.H, 4 * 64, 2);
   const int pairs = p.M * p.topk;
   p.slots_max = pairs < p.E ? pairs : p.E;
+  if (moe_use_mfma(p.M)) {
+    // one work unit per wave at least, two resident workgroups per CU at most
+    const int64_t units = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 8) + (p.SI + 127) / 128 * 8;
+    int64_t blocks = (units + kMoeGateUpWaves - 1) / kMoeGateUpWaves;
+    if (blocks > kMoeMfmaGrid) blocks = kMoeMfmaGrid;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kMoeGateUpWaves * 64);
+    if (p.M <= 4) hipLaunchKernelGGL((k_moe_gate_up_mfma<4>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_moe_gate_up_mfma<8>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  const int c = chunks_per_lane(p.H, 4 * 64, 2);
   if (p.M <= 1) return launch_gate_up_mt<1>(p, c, stream);
-  if (p.M <= 8) return launch_gate_up_mt<2>(p, c, stream);
-  return launch_gate_up_mt<4>(p, c, stream);
+  return launch_gate_up_mt<2>(p, c, stream);
 }
 
 hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
+  if (moe_use_mfma(p.M)) {
+    const int64_t tiles = (p.H + 127) / 128 * 8;
+    const dim3 grid(static_cast<unsigned>(tiles < 4096 ? tiles : 4096)), block(kMoeDownWaves * 64);
+    if (p.M <= 4) hipLaunchKernelGGL((k_moe_down_mfma<4>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_moe_down_mfma<8>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t kmax = p.I > p.SI ? p.I : p.SI;
   const int c = chunks_per_lane(kmax, 64, 4);
   return launch_down_mt<1>(p, c, stream);
