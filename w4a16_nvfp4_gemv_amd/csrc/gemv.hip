@@ -785,8 +785,9 @@ template <bool FP4, int XT, bool SILU>
 hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
-  // (one tile per workgroup at XT = 4: measured faster there)
-  if (XT > 4 && mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
+  // (one tile per workgroup at XT = 4, and for silu_mul up to XT = 8:
+  // measured faster there)
+  if (XT > 4 && !(SILU && XT <= 8) && mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
   return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
