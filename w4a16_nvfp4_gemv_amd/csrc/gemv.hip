@@ -448,17 +448,18 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // distinct banks.
 constexpr int mfma_waves(int /*XT*/) { return 4; }
 
-// Steps in flight per wave (measured: deeper rings were slower), bounded by
-// vmcnt, which counts at most 63 outstanding loads, and by the LDS ring
-// (128 KB per workgroup).  A depth that divides the steps of a wave wastes
-// nothing in the last round; K = 4096 gives 8 NVFP4 steps and 32 BF16 steps
-// per wave.
+// Steps in flight per wave, measured: 4 for NVFP4 up to 16 staged tokens,
+// 2 at 32 (a 128 KB ring would leave one workgroup per CU), 4 or 8 for BF16
+// (deeper rings were slower).  Bounded by vmcnt, which counts at most 63
+// outstanding loads, and by the LDS ring (128 KB per workgroup).  A depth
+// that divides the steps of a wave wastes nothing in the last round; K = 4096
+// gives 8 NVFP4 steps and 32 BF16 steps per wave.
 template <bool FP4, int XT, int NA, int W>
 constexpr int mfma_depth() {
   const int per = FP4 ? 2 : 1;                   // loads per A operand and step
   const int cpt = FP4 ? 16 : 4;                  // 16-byte chunks per token and step
   const int load_x = XT * cpt / 64;              // staging loads per step
-  int d = FP4 ? 4 : (XT <= 16 ? 4 : 8);
+  int d = FP4 ? (XT == 32 ? 2 : 4) : (XT <= 16 ? 4 : 8);
   while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) d /= 2;
   return d;
 }
