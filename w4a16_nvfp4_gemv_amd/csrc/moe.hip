@@ -494,9 +494,10 @@ __global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p)
 // slot is consumed, its LDS reads retired, and it is refilled with the job
 // kMoeRing ahead, so every wait counts the same loads; the last round drains
 // the ring without refilling it.  A job's results are written by the wave
-// that consumed its last step.
-constexpr int kMoeRing = 4;
-constexpr int kMoeDownRing = 4;
+// that consumed its last step.  Two steps in flight per wave measured as fast
+// as four or eight, and leave LDS for more resident waves.
+constexpr int kMoeRing = 2;
+constexpr int kMoeDownRing = 2;
 constexpr int kMoeDownWaves = 12;
 constexpr int kMoeGateUpWaves = 4;
 
