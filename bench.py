@@ -455,6 +455,45 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
             out.append({"workload": name, "M": m, "experts_per_call": round(distinct, 2), "us": round(us, 3),
                         "GBps": round(nb / us / 1e3, 1), "bytes": int(nb)})
             log(f"{name} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s ({distinct:.1f} experts)")
+    del wts
+
+    # Large-M path: dequantize into a BF16 copy, library GEMM, scale epilogue.  Timed as
+    # eager launches on one stream (the library GEMM is not captured into a graph).
+    n, k = 4096, 4096
+    base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(5, 1))
+    nc = max(2, int(budget // (n * k // 2)))
+    ws = [base["w"].to(dev) for _ in range(nc)]
+    ss = [base["s"].to(dev) for _ in range(nc)]
+    stream = torch.cuda.Stream(device=dev)
+    for m in (64, 128, 256):
+        d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(5, m))
+        x, gs = d["x"].to(dev), d["gs"].to(dev)
+        o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        wsb = lib.nvfp4_dequant_gemm_workspace_bytes(m, n, k)
+        work = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def call(i, m=m, x=x, gs=gs, o=o, wsb=wsb, work=work):
+            assert lib.nvfp4_dequant_gemm(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), ss[i % nc].data_ptr(),
+                                          gs.data_ptr(), n, 0, work.data_ptr(), wsb, o.data_ptr(),
+                                          stream.cuda_stream) == 0
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 32
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nb = algorithmic_bytes(n, k)
+        tflops = 2.0 * m * n * k / us / 1e6
+        out.append({"workload": "nvfp4_dequant_gemm", "N": n, "K": k, "M": m, "us": round(us, 3),
+                    "GBps": round(nb / us / 1e3, 1), "TFLOPs": round(tflops, 2), "bytes": nb})
+        log(f"dequant_gemm N={n} K={k} M={m:3d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s {tflops:6.1f} TFLOP/s")
+    del ws, ss
     return out
 
 

@@ -98,6 +98,33 @@ int dequantize_rows(const uint8_t *w, const uint8_t *w_scale, int64_t rows, int6
                     uint16_t *out, void *stream);
 
 /*
+ * nvfp4_dequant_gemm -- the nvfp4_gemv result for any number of tokens: the
+ * weight is dequantized once into a BF16 copy (as dequantize_rows), one BLAS
+ * GEMM forms the FP32 sums of x @ W^T, and the global scale is applied to
+ * those sums before the single BF16 rounding (linear page, function
+ * _dequant_gemm; there the scale is the GEMM's alpha).  The path beside the
+ * GEMV kernels for M beyond W4A16_MAX_M.
+ *   x, w, w_scale, global_scale, silu_mul, out   as nvfp4_gemv, any M >= 0;
+ *                x and out need only 2-byte alignment, ldx >= K.
+ *   workspace    device memory owned by the caller, 256-byte aligned, of at
+ *                least nvfp4_dequant_gemm_workspace_bytes(M, N, K) bytes; it
+ *                holds the BF16 weight copy and the FP32 sums, and its
+ *                contents are undefined afterwards.  Calls that share a
+ *                workspace must not overlap.
+ *   Needs N % 16 == 0 and K % 256 == 0 (dequantize_rows), and N % 32 == 0
+ *   with silu_mul.  The GEMM runs through rocBLAS: the first call on a device
+ *   creates that device's rocBLAS handle, which keeps rocBLAS's own device
+ *   memory until the process ends.  A GEMM failure returns W4A16_ERR_HIP.
+ * nvfp4_dequant_gemm_workspace_bytes returns the workspace size in bytes
+ * (-1 for negative or too large sizes).
+ */
+int64_t nvfp4_dequant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int nvfp4_dequant_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                       const uint8_t *w, const uint8_t *w_scale, const float *global_scale,
+                       int64_t N, int silu_mul, void *workspace, int64_t workspace_bytes,
+                       uint16_t *out, void *stream);
+
+/*
  * nvfp4_unswizzle_scales -- out[n][c] = the scale of row n, column c (= k/16)
  * read from the flat 128x4-swizzled buffer; bit-exact.  Exposes the scale
  * addressing the GEMV kernels use (the 128x4 layout named on the

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["nvfp4_gemv", "bf16_gemv", "dequantize_rows", "moe_gate_up", "moe_down_combine",
-                 "nvfp4_unswizzle_scales", "w4a16_status_string", "w4a16_last_error"]:
+                 "nvfp4_unswizzle_scales", "nvfp4_dequant_gemm", "nvfp4_dequant_gemm_workspace_bytes",
+                 "w4a16_status_string", "w4a16_last_error"]:
         assert want in names
 
 
@@ -98,6 +99,45 @@ def test_dequantize_rows_argument_errors():
     assert lib.dequantize_rows(FAKE + 4, FAKE, 32, 4096, FAKE, None) == MISALIGNED
     assert lib.dequantize_rows(None, FAKE, 32, 4096, FAKE, None) == INVALID
     assert lib.dequantize_rows(None, None, 0, 4096, None, None) == OK
+
+
+def dgemm(**kw):
+    lib = _lib.load()
+    a = dict(x=FAKE, M=64, K=4096, ldx=4096, w=FAKE, s=FAKE, gs=FAKE, N=4096, silu=0, ws=FAKE, wsb=None, out=FAKE)
+    a.update(kw)
+    wsb = a["wsb"] if a["wsb"] is not None else lib.nvfp4_dequant_gemm_workspace_bytes(a["M"], a["N"], a["K"])
+    return lib.nvfp4_dequant_gemm(a["x"], a["M"], a["K"], a["ldx"], a["w"], a["s"], a["gs"], a["N"], a["silu"],
+                                  a["ws"], wsb, a["out"], None)
+
+
+def test_dequant_gemm_workspace_size():
+    lib = _lib.load()
+    # BF16 weight copy rounded up to 256 bytes, then the FP32 sums
+    assert lib.nvfp4_dequant_gemm_workspace_bytes(64, 4096, 4096) == 4096 * 4096 * 2 + 64 * 4096 * 4
+    assert lib.nvfp4_dequant_gemm_workspace_bytes(3, 16, 256) == 16 * 256 * 2 + 3 * 16 * 4
+    assert lib.nvfp4_dequant_gemm_workspace_bytes(1, 16, 264) == (16 * 264 * 2 + 255) // 256 * 256 + 16 * 4
+    assert lib.nvfp4_dequant_gemm_workspace_bytes(-1, 16, 256) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INVALID),
+    (dict(K=4096 + 64, ldx=4096 + 64), UNSUPPORTED),  # K % 256 != 0
+    (dict(N=4100), UNSUPPORTED),         # N % 16 != 0
+    (dict(N=48, silu=1), UNSUPPORTED),   # silu needs N % 32 == 0
+    (dict(silu=3), INVALID),
+    (dict(ldx=4000), INVALID),           # ldx < K
+    (dict(wsb=1024), INVALID),           # workspace too small
+    (dict(ws=None), INVALID),
+    (dict(gs=None), INVALID),
+    (dict(ws=FAKE + 16), MISALIGNED),    # workspace 256-byte aligned
+    (dict(w=FAKE + 8), MISALIGNED),
+    (dict(x=FAKE + 1), MISALIGNED),
+    (dict(M=0, x=None, w=None, s=None, gs=None, ws=None, out=None), OK),  # M == 0: no-op
+])
+def test_dequant_gemm_argument_errors(kw, status):
+    assert dgemm(**kw) == status
+    if status != OK:
+        assert _lib.load().w4a16_last_error()
 
 
 def test_unswizzle_argument_errors():

@@ -135,6 +135,48 @@ def test_nvfp4_gemv_long_rows(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m,n,k,silu", [
+    (1, 256, 512, False),
+    (33, 256, 512, False),       # one token past the GEMV kernels
+    (64, 144, 768, False),       # ragged 128-row band
+    (200, 384, 1024, False),
+    (48, 512, 512, True),
+    (96, 4096, 4096, False),     # the sweep's weight at 96 tokens
+])
+def test_nvfp4_dequant_gemm(m, n, k, silu):
+    """Large-M path (dequantize into a BF16 copy, library GEMM with FP32 sums,
+    scale epilogue) against the GEMV oracle, whose definition it shares."""
+    _say("dequant_gemm", m, n, k, silu)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 7 * n + k)
+    out = lib.dequant_gemm(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]), silu_mul=silu)
+    torch.cuda.synchronize()
+    got = to_bits(out.cpu())
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, d["gs"][0], f"dequant_gemm silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, d["gs"][0], k, f"dequant_gemm M={m} N={n} K={k}")
+
+
+def test_nvfp4_dequant_gemm_strided_x_and_reuse():
+    """x with a row stride past K; a second call with other sizes on a fresh
+    workspace gives the same results as a call of its own."""
+    m, n, k = 40, 256, 768
+    d = synth.dense_w4a16(m, n, k, seed=4242)
+    xpad = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    xpad[:, :k] = d["x"]
+    x = dev(xpad)[:, :k]
+    assert x.stride(0) == k + 64
+    out = lib.dequant_gemm(x, dev(d["w"]), dev(d["s"]), dev(d["gs"]))
+    torch.cuda.synchronize()
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(to_bits(out.cpu()), acc, absacc, d["gs"][0], k, "dequant_gemm strided x")
+    d2 = synth.dense_w4a16(5, 128, 256, seed=4243)
+    a = to_bits(lib.dequant_gemm(dev(d2["x"]), dev(d2["w"]), dev(d2["s"]), dev(d2["gs"])).cpu())
+    b = to_bits(lib.dequant_gemm(dev(d2["x"]), dev(d2["w"]), dev(d2["s"]), dev(d2["gs"])).cpu())
+    np.testing.assert_array_equal(a, b)  # the sums do not depend on timing (no atomics)
+
+
 @pytest.mark.parametrize("m", [8, 17, 32])
 @pytest.mark.parametrize("n,k,silu", [(4224, 128, False), (4176, 192, False), (8448, 128, True), (8256, 64, True)])
 def test_nvfp4_gemv_many_row_tiles(m, n, k, silu):

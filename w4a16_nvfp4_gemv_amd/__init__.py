@@ -5,6 +5,6 @@ include/w4a16_nvfp4_gemv.h); this package only marshals torch tensors into
 its entry points.
 """
 from .ops import (  # noqa: F401
-    W4A16Error, bf16_gemv, dequantize_rows, down_combine, gate_up, gemv_kernel_name, moe_down_combine,
+    W4A16Error, bf16_gemv, dequant_gemm, dequantize_rows, down_combine, gate_up, gemv_kernel_name, moe_down_combine,
     moe_gate_up, nvfp4_gemv, nvfp4_unswizzle_scales,
 )

@@ -19,6 +19,8 @@ SIGNATURES = {
     "nvfp4_gemv": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _p]),
     "bf16_gemv": (_int, [_p, _i64, _i64, _i64, _p, _i64, _int, _p, _p]),
     "dequantize_rows": (_int, [_p, _p, _i64, _i64, _p, _p]),
+    "nvfp4_dequant_gemm_workspace_bytes": (_i64, [_i64, _i64, _i64]),
+    "nvfp4_dequant_gemm": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _i64, _p, _p]),
     "nvfp4_unswizzle_scales": (_int, [_p, _i64, _i64, _p, _p]),
     "moe_gate_up": (_int, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "moe_down_combine": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p]),

@@ -39,6 +39,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
         "-I", os.path.join(ROOT, "include"),
         *sources(), "-o", LIB + ".tmp",
+        # the library GEMM of the dequant + GEMM path
+        "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas",
     ]
     if extra:
         cmd[1:1] = extra

@@ -166,6 +166,42 @@ int dequantize_rows(const uint8_t* w, const uint8_t* w_scale, int64_t rows, int6
   return hip_status(w4a16::launch_dequantize_rows(w, w_scale, rows, K, out, static_cast<hipStream_t>(stream)));
 }
 
+int64_t nvfp4_dequant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+  return (N * K * 2 + 255) / 256 * 256 + M * N * 4;
+}
+
+int nvfp4_dequant_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
+                       const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
+                       void* workspace, int64_t workspace_bytes, uint16_t* out, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0 || ldx < K) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld N=%lld", M, N);
+  if (silu_mul != 0 && silu_mul != 1) return fail(W4A16_ERR_INVALID_ARG, "silu_mul must be 0 or 1");
+  if (N % 16 || K % 256) return fail(W4A16_ERR_UNSUPPORTED, "needs N %% 16 == 0 and K %% 256 == 0 (N=%lld K=%lld)", N, K);
+  if (silu_mul && N % 32) return fail(W4A16_ERR_UNSUPPORTED, "silu_mul needs N %% 32 == 0 (N=%lld)", N);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || ldx > kMaxDim || M * ldx > kMaxDim)
+    return fail(W4A16_ERR_UNSUPPORTED, "size too large (M=%lld N=%lld)", M, N);
+  if (M == 0) return ok();
+  if (!x || !w || !w_scale || !global_scale || !workspace || !out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+  if (workspace_bytes < nvfp4_dequant_gemm_workspace_bytes(M, N, K))
+    return fail(W4A16_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", workspace_bytes,
+                nvfp4_dequant_gemm_workspace_bytes(M, N, K));
+  if (!aligned(x, 2) || !aligned(out, 2) || !aligned(w, 16) || !aligned(w_scale, 4) || !aligned(global_scale, 4) ||
+      !aligned(workspace, 256))
+    return fail(W4A16_ERR_MISALIGNED, "x/out 2-byte, w 16-byte, w_scale 4-byte, workspace 256-byte alignment required");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* w_bf16 = static_cast<uint16_t*>(workspace);
+  float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + (N * K * 2 + 255) / 256 * 256);
+  int status = hip_status(w4a16::launch_dequantize_rows(w, w_scale, N, K, w_bf16, st));
+  if (status != W4A16_OK) return status;
+  const char* why = "library GEMM failed";
+  const hipError_t e = w4a16::gemm_bf16_f32(x, M, K, ldx, w_bf16, N, acc, st, &why);
+  if (e != hipSuccess) {
+    g_last_error = std::string("GEMM: ") + why;
+    return W4A16_ERR_HIP;
+  }
+  return hip_status(w4a16::launch_scale_epilogue(acc, global_scale, out, M, N, silu_mul, st));
+}
+
 int nvfp4_unswizzle_scales(const uint8_t* w_scale, int64_t N, int64_t K, uint8_t* out,
                            void* stream) {
   if (N < 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes N=%lld K=%lld", N, K);

@@ -54,6 +54,31 @@ __global__ __launch_bounds__(256) void k_unswizzle(const uint8_t* __restrict__ s
   }
 }
 
+// Epilogue of the dequant + GEMM path: out = bf16(acc * gs) from the FP32
+// GEMM result acc [M][N], or with silu_mul out[m][j] = bf16(silu(g) * u),
+// g = bf16(acc[m][j] * gs), u = bf16(acc[m][N/2 + j] * gs) (the same
+// epilogue as the GEMV kernels).
+__global__ __launch_bounds__(256) void k_scale_epilogue(const float* __restrict__ acc,
+                                                        const float* __restrict__ gs_ptr,
+                                                        uint16_t* __restrict__ out, int64_t M, int64_t N,
+                                                        int silu_mul) {
+  const float gs = *gs_ptr;
+  const int64_t cols = silu_mul ? N / 2 : N;
+  const int64_t total = M * cols;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t m = i / cols;
+    const int64_t j = i - m * cols;
+    if (!silu_mul) {
+      out[i] = f32_to_bf16_bits(acc[m * N + j] * gs);
+    } else {
+      const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[m * N + j] * gs));
+      const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc[m * N + cols + j] * gs));
+      out[i] = f32_to_bf16_bits(silu_f32(g) * u);
+    }
+  }
+}
+
 namespace {
 unsigned grid_for(int64_t items) {
   int64_t b = (items + 255) / 256;
@@ -73,6 +98,13 @@ hipError_t launch_dequantize_rows(const uint8_t* w, const uint8_t* s, int64_t ro
 hipError_t launch_unswizzle(const uint8_t* s, int64_t N, int64_t K, uint8_t* out,
                             hipStream_t stream) {
   hipLaunchKernelGGL(k_unswizzle, dim3(grid_for(N * (K / 16))), dim3(256), 0, stream, s, out, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_epilogue(const float* acc, const float* gs, uint16_t* out, int64_t M, int64_t N,
+                                 int silu_mul, hipStream_t stream) {
+  const int64_t items = M * (silu_mul ? N / 2 : N);
+  hipLaunchKernelGGL(k_scale_epilogue, dim3(grid_for(items)), dim3(256), 0, stream, acc, gs, out, M, N, silu_mul);
   return hipGetLastError();
 }
 

@@ -1,17 +1,18 @@
 // Dense small-M GEMV kernels for gfx950: out = bf16(fp32(x @ W^T) * gs).
 //
 // Three kernel families serve the same entry points:
-//   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns and M <= 4 tokens.
-//     VALU dot products over exactly decoded BF16 pairs (v_dot2_f32_bf16);
-//     lanes own interleaved 8-k chunks so that every load instruction of a
-//     wave reads one contiguous stretch, and a permlane reduce-scatter sums
-//     the lanes.
+//   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns and M <= 2 tokens
+//     (up to 4 when the VALU path is forced).  VALU dot products over exactly
+//     decoded BF16 pairs (v_dot2_f32_bf16); lanes own interleaved 8-k chunks
+//     so that every load instruction of a wave reads one contiguous stretch,
+//     and a permlane reduce-scatter sums the lanes.
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
 //     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 and
 //     NVFP4 rows longer than 16384 columns at M <= 2.
 //   * k_gemv_mfma -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
-//     weight rows of a tile are the A operand, up to 16 tokens the B operand.
-//     The waves of a workgroup split K and reduce through LDS.
+//     weight rows of a tile are the A operand, up to 16 tokens the B operand,
+//     staged through an LDS ring.  The waves of a workgroup split K and
+//     reduce through LDS.
 // All of them stream every weight byte exactly once with buffer loads, and
 // all apply the FP32 global scale to the FP32 sum before the single BF16
 // rounding (nvfp4_gemv page, module docstring "Numerics").
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
       const bool kv = sv && k < static_cast<uint32_t>(p.K);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
-        const bool ok = rv[a] && kv;
+        const bool ok = rv[a] && kv;  // (a select here measured faster than off_if)
         if constexpr (FP4) {
           sb[d][a] = bload4(rs, ok ? static_cast<uint32_t>(scale_word_offset(rows[a], k / 64, p.tiles)) : kOutOfRange);
           wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k / 2 : kOutOfRange);

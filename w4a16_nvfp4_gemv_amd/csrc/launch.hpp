@@ -36,6 +36,11 @@ hipError_t launch_dequantize_rows(const uint8_t* w, const uint8_t* s, int64_t ro
                                   uint16_t* out, hipStream_t stream);
 hipError_t launch_unswizzle(const uint8_t* s, int64_t N, int64_t K, uint8_t* out,
                             hipStream_t stream);
+hipError_t launch_scale_epilogue(const float* acc, const float* gs, uint16_t* out, int64_t M, int64_t N,
+                                 int silu_mul, hipStream_t stream);
+// out = x @ w_bf16^T as FP32 [M][N] by one BLAS GEMM (no scaling).
+hipError_t gemm_bf16_f32(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w_bf16, int64_t N,
+                         float* acc, hipStream_t stream, const char** why);
 
 struct MoeGateUpParams {
   const uint16_t* x;      // bf16 [M][H]

@@ -88,6 +88,32 @@ def bf16_gemv(x: torch.Tensor, weight: torch.Tensor, silu_mul: bool = False,
     return out
 
 
+def dequant_gemm(x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor,
+                 global_scale: torch.Tensor, silu_mul: bool = False) -> torch.Tensor:
+    """The nvfp4_gemv result for any number of tokens, by dequantize + library GEMM."""
+    x = _x2d(x)
+    if weight.dtype != torch.uint8 or weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous uint8 [N, K/2] tensor")
+    m, k = x.shape[0], weight.shape[1] * 2
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weight needs K={k}")
+    n = weight.shape[0]
+    gs = global_scale.reshape(1)
+    if gs.dtype != torch.float32:
+        raise ValueError("global_scale must be float32")
+    scale = _flat_u8(weight_scale)
+    lib = _lib.load()
+    ws_bytes = lib.nvfp4_dequant_gemm_workspace_bytes(m, n, k)
+    if ws_bytes < 0:
+        raise ValueError(f"sizes out of range (M={m} N={n} K={k})")
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    out = torch.empty((m, n // 2 if silu_mul else n), dtype=torch.bfloat16, device=x.device)
+    st = lib.nvfp4_dequant_gemm(x.data_ptr(), m, k, x.stride(0), weight.data_ptr(), scale.data_ptr(), gs.data_ptr(),
+                                n, int(bool(silu_mul)), workspace.data_ptr(), ws_bytes, out.data_ptr(), _stream(x))
+    _check(st, "nvfp4_dequant_gemm")
+    return out
+
+
 def dequantize_rows(weight: torch.Tensor, weight_scale: torch.Tensor) -> torch.Tensor:
     """Exact BF16 e2m1 * e4m3 of every weight row (global scale not applied)."""
     if weight.dtype != torch.uint8 or weight.dim() != 2 or not weight.is_contiguous():
