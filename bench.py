@@ -457,6 +457,27 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
             log(f"{name} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s ({distinct:.1f} experts)")
     del wts
 
+    # The MFMA GEMV past 32 tokens (up to four 16-token tiles)
+    for n, k in ((4096, 4096), (6144, 4096)):
+        base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(6, 1, n))
+        nc = max(2, int(budget // (n * k // 2)))
+        ws = [base["w"].to(dev) for _ in range(nc)]
+        ss = [base["s"].to(dev) for _ in range(nc)]
+        for m in (48, 64):
+            d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(6, m, n))
+            x, gs = d["x"].to(dev), d["gs"].to(dev)
+            o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+            def f(i, h, m=m, x=x, gs=gs, o=o, n=n, k=k):
+                assert lib.nvfp4_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), ss[i % nc].data_ptr(),
+                                      gs.data_ptr(), n, 0, o.data_ptr(), h) == 0
+            us = time_graph(f, 32)
+            nb = algorithmic_bytes(n, k)
+            out.append({"workload": "nvfp4_gemv", "N": n, "K": k, "M": m, "kernel": gemv_kernel_name(m, n, k),
+                        "us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb})
+            log(f"nvfp4_gemv N={n} K={k} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s")
+        del ws, ss
+
     # Large-M path: dequantize into a BF16 copy, library GEMM, scale epilogue.  Timed as
     # eager launches on one stream (the library GEMM is not captured into a graph).
     n, k = 4096, 4096

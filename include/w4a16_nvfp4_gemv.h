@@ -29,8 +29,9 @@
  * the FP32 accumulator and the result is rounded to BF16 once (round to
  * nearest even).  The FP32 summation order is unspecified.
  *
- * Shape limits shared by the GEMV entry points: 0 <= M <= 32 tokens (M == 0
- * is a successful no-op), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
+ * Shape limits shared by the GEMV entry points: 0 <= M <= 64 tokens (M == 0
+ * is a successful no-op; the pages' kernels stop at 32 tokens, the MFMA
+ * kernels here take up to four 16-token tiles), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
  * Pointer alignment: activations, weights and scale buffers 16 bytes,
  * global scale 4 bytes, outputs 2 bytes; the row stride ldx of x is a
  * multiple of 8 elements.  Each of x, the weight and the scale buffer must
@@ -56,8 +57,9 @@ extern "C" {
 #define W4A16_ERR_UNSUPPORTED 3   /* valid request outside the supported shapes */
 #define W4A16_ERR_HIP 4           /* the HIP runtime refused a launch */
 
-/* Largest token count of the GEMV entry points. */
-#define W4A16_MAX_M 32
+/* Largest token count of the GEMV entry points, and of the MoE pair. */
+#define W4A16_MAX_M 64
+#define W4A16_MOE_MAX_M 32
 
 /*
  * nvfp4_gemv -- out[M][N] = bf16(fp32(x @ dequant(W)^T) * global_scale).
@@ -150,7 +152,7 @@ int nvfp4_unswizzle_scales(const uint8_t *w_scale, int64_t N, int64_t K, uint8_t
  *            gssh FP32 [1] (device).
  *   sact     bf16 [M][SI] output: the nvfp4_gemv silu_mul result of the
  *            shared expert.
- * Limits: 0 <= M <= 32 (M == 0 is a no-op), 1 <= topk <= 16, E >= 1,
+ * Limits: 0 <= M <= W4A16_MOE_MAX_M (M == 0 is a no-op), 1 <= topk <= 16, E >= 1,
  * H % 64 == 0, I % 16 == 0, SI % 16 == 0.
  */
 int moe_gate_up(const uint16_t *x, int64_t M, int64_t H, const int32_t *ids, int64_t topk,

@@ -59,7 +59,7 @@ def gemv(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(M=33), UNSUPPORTED),
+    (dict(M=65), UNSUPPORTED),
     (dict(M=-1), INVALID),
     (dict(K=4032 + 32), UNSUPPORTED),    # K % 64 != 0
     (dict(K=0), INVALID),
@@ -87,7 +87,7 @@ def test_nvfp4_gemv_argument_errors(kw, status):
 
 def test_bf16_gemv_argument_errors():
     lib = _lib.load()
-    assert lib.bf16_gemv(FAKE, 33, 4096, 4096, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
+    assert lib.bf16_gemv(FAKE, 65, 4096, 4096, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
     assert lib.bf16_gemv(FAKE, 1, 4104, 4104, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED  # K % 16
     assert lib.bf16_gemv(FAKE, 0, 4096, 4096, None, 4096, 0, None, None) == OK
 
@@ -180,7 +180,7 @@ def test_gemv_kernel_name_query(monkeypatch):
         assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_vchunk<{m}, false,")
         assert gemv_kernel_name(m, 28672, 4096, silu_mul=True).startswith(f"k_gemv_vchunk<{m}, true,")
     # the MFMA kernels are named by the token rows they stage per step
-    for m, xt in ((3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32)):
+    for m, xt in ((3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 6144, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 16, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
@@ -188,6 +188,8 @@ def test_gemv_kernel_name_query(monkeypatch):
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "valu")
     assert gemv_kernel_name(4, 4096, 4096).startswith("k_gemv_vchunk<4, false,")
-    for bad in (dict(m=0, n=16, k=64), dict(m=33, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
+    assert gemv_kernel_name(64, 6144, 4096).endswith(", 2>")  # two row tiles per workgroup
+    assert gemv_kernel_name(64, 2 * 6144, 4096, silu_mul=True).endswith(", 1>")  # LDS: one with silu_mul
+    for bad in (dict(m=0, n=16, k=64), dict(m=65, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
         with pytest.raises(W4A16Error):
             gemv_kernel_name(bad["m"], bad["n"], bad["k"])

@@ -135,9 +135,39 @@ def test_nvfp4_gemv_long_rows(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [33, 47, 64])
+@pytest.mark.parametrize("n,k,silu", [(256, 512, False), (144, 320, False), (4224, 128, False),
+                                      (512, 256, True), (4096, 4096, False)])
+def test_nvfp4_gemv_up_to_64_tokens(m, n, k, silu):
+    """33..64 tokens: four 16-token tiles staged per step (ragged last tile,
+    ragged K, ragged 128-row band, more tiles than compute units, silu_mul,
+    the sweep's weight)."""
+    _say("nvfp4_gemv 64 tokens", m, n, k, silu)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 3 * n + k)
+    got = run_nvfp4(d, n, silu=silu)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, d["gs"][0], f"silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [40, 64])
+@pytest.mark.parametrize("n,k,silu", [(256, 512, False), (96, 144, False), (512, 256, True)])
+def test_bf16_gemv_up_to_64_tokens(m, n, k, silu):
+    _say("bf16_gemv 64 tokens", m, n, k, silu)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 5 * n + k)
+    got = run_bf16(d, silu=silu)
+    want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, 1.0, f"bf16 silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("m,n,k,silu", [
     (1, 256, 512, False),
-    (33, 256, 512, False),       # one token past the GEMV kernels
+    (33, 256, 512, False),       # past the pages' 32-token GEMV
     (64, 144, 768, False),       # ragged 128-row band
     (200, 384, 1024, False),
     (48, 512, 512, True),
@@ -252,7 +282,7 @@ def test_nvfp4_gemv_is_deterministic(m):
 
 
 def test_nvfp4_gemv_rejects_bad_shapes():
-    d = synth.dense_w4a16(33, 256, 512, seed=1)
+    d = synth.dense_w4a16(65, 256, 512, seed=1)  # one token past the limit
     with pytest.raises(lib.W4A16Error):
         lib.nvfp4_gemv(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]))
 

@@ -217,7 +217,7 @@ int moe_gate_up(const uint16_t* x, int64_t M, int64_t H, const int32_t* ids, int
                 int64_t I, uint16_t* act, const uint8_t* wsh, const uint8_t* ssh,
                 const float* gssh, int64_t SI, uint16_t* sact, void* stream) {
   if (M < 0 || H <= 0 || topk <= 0 || E <= 0 || I <= 0 || SI <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld H=%lld", M, H);
-  if (M > W4A16_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
+  if (M > W4A16_MOE_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
   if (H % 64 || I % 16 || SI % 16) return fail(W4A16_ERR_UNSUPPORTED, "needs H %% 64, I %% 16, SI %% 16 == 0 (H=%lld I=%lld)", H, I);
   if (H > kMaxDim || I > kMaxDim / 2 || SI > kMaxDim / 2 || E > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
   if (M == 0) return ok();
@@ -259,7 +259,7 @@ int moe_down_combine(const uint16_t* act, const int32_t* ids, const float* tw, i
                      const uint8_t* wsd, const uint8_t* ssd, const float* gssd, int64_t SI,
                      uint16_t* out, void* stream) {
   if (M < 0 || H <= 0 || topk <= 0 || E <= 0 || I <= 0 || SI <= 0) return fail(W4A16_ERR_INVALID_ARG, "bad sizes M=%lld H=%lld", M, H);
-  if (M > W4A16_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
+  if (M > W4A16_MOE_MAX_M || topk > 16) return fail(W4A16_ERR_UNSUPPORTED, "M=%lld topk=%lld outside limits", M, topk);
   if (H % 16 || I % 64 || SI % 64) return fail(W4A16_ERR_UNSUPPORTED, "needs H %% 16, I %% 64, SI %% 64 == 0 (I=%lld SI=%lld)", I, SI);
   if (H > kMaxDim || I > kMaxDim || SI > kMaxDim || E > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
   if (M == 0) return ok();

@@ -450,8 +450,8 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 constexpr int mfma_waves(int /*XT*/) { return 4; }
 
 // Steps in flight per wave, measured: 4 for NVFP4 up to 16 staged tokens,
-// 2 at 32 (a 128 KB ring would leave one workgroup per CU), 4 or 8 for BF16
-// (deeper rings were slower).  Bounded by vmcnt, which counts at most 63
+// 2 at 32 (a 128 KB ring would leave one workgroup per CU) and at 64, 4 or 8
+// for BF16 (deeper rings were slower).  Bounded by vmcnt, which counts at most 63
 // outstanding loads, and by the LDS ring (128 KB per workgroup).  A depth
 // that divides the steps of a wave wastes nothing in the last round; K = 4096
 // gives 8 NVFP4 steps and 32 BF16 steps per wave.
@@ -460,12 +460,12 @@ constexpr int mfma_depth() {
   const int per = FP4 ? 2 : 1;                   // loads per A operand and step
   const int cpt = FP4 ? 16 : 4;                  // 16-byte chunks per token and step
   const int load_x = XT * cpt / 64;              // staging loads per step
-  int d = FP4 ? (XT == 32 ? 2 : 4) : (XT <= 16 ? 4 : 8);
+  int d = FP4 ? (XT >= 32 ? 2 : 4) : (XT <= 16 ? 4 : 8);
   while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) d /= 2;
   return d;
 }
 
-// XT: token rows staged per step (4, 8, 16 or 32; 4 and 8 only for NVFP4,
+// XT: token rows staged per step (4, 8, 16, 32 or 64; 4 and 8 only for NVFP4,
 // whose step segment is 256 bytes per token).  With XT < 16 the fragment
 // lanes of tokens XT..15 read the rows of tokens 0..XT-1 again: those MFMA
 // columns are never stored.
@@ -788,8 +788,11 @@ hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   // (one tile per workgroup at XT = 4, and for silu_mul up to XT = 8:
-  // measured faster there)
-  if (XT > 4 && !(SILU && XT <= 8) && mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
+  // measured faster there; with silu_mul at XT = 64 a second tile's partial
+  // sums would not fit in LDS beside the ring)
+  if constexpr (XT < 64 || !SILU) {
+    if (XT > 4 && !(SILU && XT <= 8) && mfma_row_tiles(tiles) == 2) return launch_mfma_rt<FP4, XT, SILU, 2>(p, stream);
+  }
   return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
@@ -814,7 +817,8 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   if (FP4 && p.M <= 4) return launch_mfma<FP4, FP4 ? 4 : 16, SILU>(p, stream);
   if (FP4 && p.M <= 8) return launch_mfma<FP4, FP4 ? 8 : 16, SILU>(p, stream);
   if (p.M <= 16) return launch_mfma<FP4, 16, SILU>(p, stream);
-  return launch_mfma<FP4, 32, SILU>(p, stream);
+  if (p.M <= 32) return launch_mfma<FP4, 32, SILU>(p, stream);
+  return launch_mfma<FP4, 64, SILU>(p, stream);
 }
 
 }  // namespace
