@@ -431,9 +431,11 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 //
 // A workgroup takes RT row tiles (plus the matching up tiles with silu_mul);
 // its mfma_waves(XT) waves split K into contiguous slices and meet in LDS at the
-// end.  A step is 128 k for NVFP4 (one 16-byte load per lane = 32 codes
-// feeding 4 MFMAs) and 32 k for BF16 (one 16-byte load per lane = 8 weights
-// feeding 1 MFMA).  Each wave keeps D steps in flight in a ring: while the
+// end.  A step is 128 k and feeds 4 MFMAs per A operand and token tile.
+// NVFP4: lane (r, g) loads 32 codes of row r, k = 32g .. 32g+31, in one
+// 16-byte load; fragment j is k = 32g+8j .. +7.  BF16: lane (r, g) makes four
+// 16-byte loads, fragment j = k 32j+8g .. +7, so that every load of the wave
+// reads 64 contiguous bytes of each of its 16 rows.  Each wave keeps D steps in flight in a ring: while the
 // ring has later steps to fetch, every slot is refilled as soon as it is
 // consumed, so each wait is the same in-order count; the last round drains
 // the ring without refilling it.
@@ -443,44 +445,42 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 // a compute unit.  Loaded straight into B fragments, a 1 KB load would touch
 // 16 token rows and 32 cache lines.  Here each 16-byte load goes straight
 // into LDS and covers whole token segments of one step (4 tokens x 256
-// bytes for NVFP4, 16 x 64 for BF16), and the fragments are then read with
-// ds_read_b128.  Chunk c of a token's segment sits at position c ^ swz(token),
+// bytes), and the fragments are then read with ds_read_b128.  Chunk c of a token's segment sits at position c ^ swz(token),
 // so the 8 or 16 lanes that a fragment read serves in one LDS pass hit
 // distinct banks.
 constexpr int mfma_waves(int /*XT*/) { return 4; }
 
-// Steps in flight per wave, measured: 4 for NVFP4 up to 16 staged tokens,
-// 2 at 32 (a 128 KB ring would leave one workgroup per CU) and at 64, 4 or 8
-// for BF16 (deeper rings were slower).  Bounded by vmcnt, which counts at most 63
-// outstanding loads, and by the LDS ring (128 KB per workgroup).  A depth
-// that divides the steps of a wave wastes nothing in the last round; K = 4096
-// gives 8 NVFP4 steps and 32 BF16 steps per wave.
+// Steps in flight per wave, measured: 4 up to 16 staged tokens, 2 at 32 (a
+// 128 KB ring would leave one workgroup per CU) and at 64 (deeper rings were
+// slower).  Bounded by vmcnt, which counts at most 63 outstanding loads, and by
+// the LDS ring (128 KB per workgroup).  A depth that divides the steps of a
+// wave wastes nothing in the last round; K = 4096 gives 8 steps per wave.
 template <bool FP4, int XT, int NA, int W>
 constexpr int mfma_depth() {
-  const int per = FP4 ? 2 : 1;                   // loads per A operand and step
-  const int cpt = FP4 ? 16 : 4;                  // 16-byte chunks per token and step
+  const int per = FP4 ? 2 : 4;                   // loads per A operand and step
+  const int cpt = 16;                            // 16-byte chunks per token and step
   const int load_x = XT * cpt / 64;              // staging loads per step
-  int d = FP4 ? (XT >= 32 ? 2 : 4) : (XT <= 16 ? 4 : 8);
+  int d = XT >= 32 ? 2 : 4;
   while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) d /= 2;
   return d;
 }
 
-// XT: token rows staged per step (4, 8, 16, 32 or 64; 4 and 8 only for NVFP4,
-// whose step segment is 256 bytes per token).  With XT < 16 the fragment
+// XT: token rows staged per step (4, 8, 16, 32 or 64).  With XT < 16 the fragment
 // lanes of tokens XT..15 read the rows of tokens 0..XT-1 again: those MFMA
 // columns are never stored.
 template <bool FP4, int XT, bool SILU, int RT>
 __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvParams p) {
   constexpr int NT = (XT + 15) / 16;        // token tiles (B operands)
   constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
-  constexpr int KSTEP = FP4 ? 128 : 32;     // k per step
-  constexpr int NJ = FP4 ? 4 : 1;           // MFMAs per step per A operand and token tile
+  constexpr int KSTEP = 128;                // k per step
+  constexpr int NJ = 4;                     // MFMAs per step per A operand and token tile
   constexpr int W = mfma_waves(XT);
   constexpr int D = mfma_depth<FP4, XT, NA, W>();  // steps in flight per wave
   constexpr int CPT = KSTEP * 2 / 16;       // 16-byte activation chunks per token and step
   constexpr int LX = XT * CPT / 64;         // staging loads per step
   static_assert(XT * CPT % 64 == 0, "a staging load covers whole token segments");
-  constexpr int PER = FP4 ? 2 : 1;          // weight-side loads per A operand and step
+  constexpr int PER = FP4 ? 2 : 4;          // weight-side loads per A operand and step
+  constexpr int WL = FP4 ? 1 : 4;           // 16-byte weight loads per A operand and step
   constexpr int L = LX + NA * PER;          // loads per step
   // loads issued after a step's staging loads while it is the oldest in a full ring
   constexpr int FULL_AFTER = NA * PER + (D - 1) * L;
@@ -495,8 +495,7 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
   const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
   const int64_t steps_total = (p.K + KSTEP - 1) / KSTEP;
   const int64_t spw = (steps_total + W - 1) / W;       // steps per wave
-  const int64_t st0 = wave * spw;
-  const int64_t nst = st0 < steps_total ? (steps_total - st0 < spw ? steps_total - st0 : spw) : 0;
+  static_assert((W & (W - 1)) == 0, "the slice rotation below needs a power-of-two wave count");
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
   const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
@@ -513,6 +512,13 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
   }
 
   for (int64_t tile = xcd_logical_block(); tile < p.units; tile += gridDim.x) {
+    // This wave's K slice.  From 8 staged tokens on, the slices rotate with
+    // the tile, so that the workgroups of one die do not all stream the same
+    // activation slice at the same time (measured 2-6% faster at 8..32 tokens,
+    // and slower at 4).
+    const int slice = XT >= 8 ? (wave + static_cast<int>(tile & (W - 1))) & (W - 1) : wave;
+    const int64_t st0 = slice * spw;
+    const int64_t nst = st0 < steps_total ? (steps_total - st0 < spw ? steps_total - st0 : spw) : 0;
     // A operand a: row tile tile*RT + a % RT, the up half for a >= RT
     int64_t rows[NA];
     bool rv[NA];
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
         rv[RT + a] = rv[a];
       }
     }
-    u32x4 wb[D][NA];
+    u32x4 wb[D][NA][WL];
     uint32_t sb[D][NA];
     auto issue = [&](int d, int64_t st) {
       const bool sv = st < nst;
@@ -542,11 +548,19 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
       for (int a = 0; a < NA; ++a) {
         const bool ok = rv[a] && kv;  // (a select here measured faster than off_if)
         if constexpr (FP4) {
+          // K % 64 == 0: the lane's 32 codes are all in range or all out
           sb[d][a] = bload4(rs, ok ? static_cast<uint32_t>(scale_word_offset(rows[a], k / 64, p.tiles)) : kOutOfRange);
-          wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k / 2 : kOutOfRange);
+          wb[d][a][0] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k / 2 : kOutOfRange);
         } else {
+          // load j: 8 weights at k + 32j (each load of the wave reads 64
+          // contiguous bytes of 16 rows); K % 16 == 0, so each 8-weight
+          // fragment is in range or out as a whole
           sb[d][a] = 0;
-          wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k * 2 : kOutOfRange);
+#pragma unroll
+          for (int j = 0; j < WL; ++j) {
+            const bool okj = rv[a] && sv && k + 32 * j < static_cast<uint32_t>(p.K);
+            wb[d][a][j] = bload16_nt(rw, okj ? static_cast<uint32_t>(rows[a]) * row_bytes + (k + 32 * j) * 2 : kOutOfRange);
+          }
         }
       }
     };
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const int t = (16 * n + r) & (XT - 1);
-          xf[j][n] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, FP4 ? 4 * g + j : g)];
+          xf[j][n] = xl_slot<W * SLOT>(d)[wave * SLOT + t * CPT + xl_pos<CPT>(t, FP4 ? 4 * g + j : 4 * j + g)];
         }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -578,9 +592,9 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
         for (int a = 0; a < NA; ++a) {
           bf16x8 av;
           if constexpr (FP4) {
-            av = fp4_a_fragment(wb[d][a], sb[d][a], g, j);
+            av = fp4_a_fragment(wb[d][a][0], sb[d][a], g, j);
           } else {
-            av = __builtin_bit_cast(bf16x8, wb[d][a]);
+            av = __builtin_bit_cast(bf16x8, wb[d][a][j]);
           }
 #pragma unroll
           for (int n = 0; n < NT; ++n)
@@ -814,8 +828,8 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
     return launch_valu<FP4, 2, SILU>(p, lpq, stream);
   }
   p.tiles = p.K / 64;
-  if (FP4 && p.M <= 4) return launch_mfma<FP4, FP4 ? 4 : 16, SILU>(p, stream);
-  if (FP4 && p.M <= 8) return launch_mfma<FP4, FP4 ? 8 : 16, SILU>(p, stream);
+  if (p.M <= 4) return launch_mfma<FP4, 4, SILU>(p, stream);
+  if (p.M <= 8) return launch_mfma<FP4, 8, SILU>(p, stream);
   if (p.M <= 16) return launch_mfma<FP4, 16, SILU>(p, stream);
   if (p.M <= 32) return launch_mfma<FP4, 32, SILU>(p, stream);
   return launch_mfma<FP4, 64, SILU>(p, stream);
