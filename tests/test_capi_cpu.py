@@ -184,6 +184,9 @@ def test_gemv_kernel_name_query(monkeypatch):
         assert gemv_kernel_name(m, 6144, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
+    # BF16 at one token: MFMA up to K = 8192, the VALU kernel beyond
+    assert gemv_kernel_name(1, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
+    assert gemv_kernel_name(1, 4096, 14336, weight_fp4=False).startswith("k_gemv_valu<false, 1,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "valu")
