@@ -272,6 +272,75 @@ def test_nvfp4_gemv_row_stride_and_zero_tokens():
     assert tuple(empty.shape) == (0, n)
 
 
+@pytest.mark.parametrize("m", [1, 2, 5, 17, 40])
+def test_gemv_row_strided_activations_every_family(m):
+    """x with a row stride past K (ldx = K + 64) on each kernel family: the
+    VALU kernels (1, 2 tokens), and the MFMA tiles staging 8, 32 and 64
+    tokens; NVFP4 and BF16 weights."""
+    n, k = 272, 1088
+    d = synth.dense_w4a16(m, n, k, seed=90 + m)
+    wide = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    wide[:, :k] = d["x"]
+    xv = dev(wide)[:, :k]
+    out = to_bits(lib.nvfp4_gemv(xv, dev(d["w"]), dev(d["s"]), dev(d["gs"])).cpu())
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(out, acc, absacc, d["gs"][0], k, f"strided x nvfp4 M={m}")
+    b = synth.dense_bf16(m, n, k, seed=95 + m)
+    wide[:, :k] = b["x"]
+    xv = dev(wide)[:, :k]
+    out = to_bits(lib.bf16_gemv(xv, dev(b["w"])).cpu())
+    _, acc, absacc = oracle.bf16_gemv(b["x"], b["w"])
+    check_gemv(out, acc, absacc, 1.0, k, f"strided x bf16 M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8, 32])
+def test_gemv_and_moe_in_hip_graph_replays(m):
+    """The calls captured in a HIP graph (as the benchmark runs them) give the
+    eager results bit for bit on every replay, with eager work and
+    synchronisation between the replays."""
+    n, k = 512, 1024
+    d = synth.dense_w4a16(m, n, k, seed=60 + m)
+    x, w, sc, gs = dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"])
+    e, topk, h, inter, si = 8, 4, 256, 128, 128
+    wts = {kk: dev(v) for kk, v in synth.moe_weights(e, h, inter, si, seed=70 + m).items()}
+    tok = {kk: dev(v) for kk, v in synth.moe_tokens(m, h, e, topk, seed=80 + m).items()}
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    fused = torch.empty((m, n // 2), dtype=torch.bfloat16, device=DEV)
+    act = torch.empty((m * topk, inter), dtype=torch.bfloat16, device=DEV)
+    sact = torch.empty((m, si), dtype=torch.bfloat16, device=DEV)
+    mo = torch.empty((m, h), dtype=torch.bfloat16, device=DEV)
+
+    def calls():
+        out.copy_(lib.nvfp4_gemv(x, w, sc, gs))
+        fused.copy_(lib.nvfp4_gemv(x, w, sc, gs, silu_mul=True))
+        lib.moe_gate_up(tok["x"], tok["ids"], wts["w1"], wts["w1_sf"], wts["alpha"], act, wts["wsh"],
+                        wts["ssh"], wts["gssh"], sact)
+        lib.moe_down_combine(act, tok["ids"], tok["tw"], wts["w2"], wts["w2_sf"], wts["alpha2"], sact,
+                             wts["wsd"], wts["ssd"], wts["gssd"], mo)
+
+    calls()
+    torch.cuda.synchronize()
+    want = [to_bits(t.cpu()) for t in (out, fused, act, sact, mo)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):  # warm the allocator on the capture stream
+        calls()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    for rep in range(3):
+        for t in (out, fused, act, sact, mo):
+            t.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [to_bits(t.cpu()) for t in (out, fused, act, sact, mo)]
+        for name, a, b in zip(("gemv", "silu", "act", "sact", "moe out"), got, want):
+            assert np.array_equal(a, b), f"graph replay {rep}: {name} differs from the eager call (M={m})"
+
+
 @pytest.mark.parametrize("m", [1, 8, 32])
 def test_nvfp4_gemv_is_deterministic(m):
     """Split-K partials are added in split order, so repeated calls agree bit for bit."""
