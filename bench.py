@@ -289,23 +289,28 @@ def main() -> int:
 
     # ---------------------------------------------------------------- per call
     def time_graph(launch_i, n_launch: int) -> float:
-        """µs per launch of a graph of n_launch launches, HIP events on the replay stream."""
+        """µs per launch of a graph of n_launch launches, HIP events on the
+        replay stream: the median of 3 rounds of 5 replays, after 2 untimed
+        replays (the first replays of a new graph run measurably slower)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
             h = torch.cuda.current_stream().cuda_stream
             for i in range(n_launch):
                 launch_i(i, h)
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 5
-        a.record()
-        for _ in range(reps):
+        for _ in range(2):
             g.replay()
-        b.record()
         torch.cuda.synchronize()
+        reps, rounds = 5, []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            rounds.append(a.elapsed_time(b) * 1e3 / (reps * n_launch))
         del g
-        return a.elapsed_time(b) * 1e3 / (reps * n_launch)
+        return sorted(rounds)[1]
 
     per_call = []
     L = args.per_call_launches
