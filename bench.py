@@ -64,12 +64,14 @@ GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp
 
 
 def source_digest() -> str:
-    """Digest of the dense GEMV kernel sources: counter figures taken on other sources are stale."""
+    """Digest of the code of the dense GEMV kernel sources (line comments and
+    blank lines left out): counter figures taken on other code are stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_nvfp4_gemv_amd", "csrc")
     for f in GEMV_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = [line.split("//", 1)[0].rstrip() for line in fh]
+        h.update(f.encode() + "\n".join(c for c in code if c).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,8 +7,8 @@
 //     so that every load instruction of a wave reads one contiguous stretch,
 //     and a permlane reduce-scatter sums the lanes.
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
-//     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 and
-//     NVFP4 rows longer than 16384 columns at M <= 2.
+//     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 beyond
+//     8192 columns and NVFP4 rows longer than 16384 columns at M <= 2.
 //   * k_gemv_mfma -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
 //     weight rows of a tile are the A operand, up to 16 tokens the B operand,
 //     staged through an LDS ring.  The waves of a workgroup split K and
