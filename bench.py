@@ -63,11 +63,11 @@ def log(*a):
 GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp", "launch.hpp"]
 
 
-def source_digest() -> str:
+def source_digest(csrc: str | None = None) -> str:
     """Digest of the code of the dense GEMV kernel sources (line comments and
     blank lines left out): counter figures taken on other code are stale."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "w4a16_nvfp4_gemv_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "w4a16_nvfp4_gemv_amd", "csrc")
     for f in GEMV_SOURCES:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             code = [line.split("//", 1)[0].rstrip() for line in fh]
@@ -145,7 +145,7 @@ def _short_kernel(name: str) -> str:
     return s.split("::")[-1] if s.startswith("w4a16::") else s
 
 
-def ingest_counters(fetch_csv: str, write_csv: str) -> int:
+def ingest_counters(fetch_csv: str, write_csv: str, out_file: str = TRAFFIC_FILE) -> int:
     """Per-kernel HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE
     counter_collection.csv of the counter pass, each counter scaled by what it
     reads for the 64 MiB copy of the same run; writes TRAFFIC_FILE."""
@@ -179,8 +179,8 @@ def ingest_counters(fetch_csv: str, write_csv: str) -> int:
                            "fetch_kib_per_copy": round(fetch_copy, 3), "fetch_scale": round(fscale, 5),
                            "write_kib_per_copy": round(write_copy, 3), "write_scale": round(wscale, 5)},
            "kernels": kernels}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_file), exist_ok=True)
+    with open(out_file, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
     return 0
