@@ -22,6 +22,10 @@ The "extras" list times the other workloads of the family (fused gate|up
 SiLU GEMV, BF16-weight GEMV, MoE decode pair) the same way; they are not
 part of the step.
 
+A third helper mode times every dispatch path of the dense GEMV per token
+count (the evidence behind the fixed dispatch rule):
+    python bench.py --dispatch-table
+
 Two helper modes feed profiles/traffic_counters.json:
     rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --counter-pass
     rocprofv3 --pmc WRITE_SIZE ... -- python3 bench.py --counter-pass
@@ -186,6 +190,113 @@ def ingest_counters(fetch_csv: str, write_csv: str, out_file: str = TRAFFIC_FILE
     return 0
 
 
+# ---------------------------------------------------------------- timing
+def graph_us_per_launch(torch, cap, launch_i, n_launch: int) -> float:
+    """µs per launch of a graph of n_launch launches captured on `cap`, HIP
+    events on the replay stream: the median of 3 rounds of 5 replays, after
+    2 untimed replays (the first replays of a new graph run measurably
+    slower)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(n_launch):
+            launch_i(i, h)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    reps, rounds = 5, []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        rounds.append(a.elapsed_time(b) * 1e3 / (reps * n_launch))
+    del g
+    return sorted(rounds)[1]
+
+
+DISPATCH_M = [1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64]
+
+
+def dispatch_table() -> int:
+    """Per (N, K, M) of the dense sweep shapes: the µs per call of the default
+    dispatch and of each path forced with W4A16_GEMV_PATH, with the kernel
+    each one launches (graphs of 64 launches over 60 rotating weight copies,
+    timed in turns: the median of 3 rounds).  One JSON line per shape, then a
+    summary line."""
+    import torch
+
+    import synth
+    from w4a16_nvfp4_gemv_amd import _lib, gemv_kernel_name
+
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cap = torch.cuda.Stream()
+    n_copies = 60
+    rows, best_default = [], 0
+    for n, k, variant in SHAPES:
+        base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(1, 1, variant))
+        ws = [base["w"].to(dev) for _ in range(n_copies)]
+        ss = [base["s"].to(dev) for _ in range(n_copies)]
+        for m in DISPATCH_M:
+            d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, variant))
+            x, gs = d["x"].to(dev), d["gs"].to(dev)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+            def launch(i, h):
+                st = lib.nvfp4_gemv(x.data_ptr(), m, k, x.stride(0), ws[i % n_copies].data_ptr(),
+                                    ss[i % n_copies].data_ptr(), gs.data_ptr(), n, 0, out.data_ptr(), h)
+                if st != 0:
+                    raise RuntimeError(f"nvfp4_gemv failed: {lib.w4a16_last_error().decode()}")
+            rec = {"N": n, "K": k, "M": m}
+            graphs = {}
+            for path in ("default", "valu", "mfma"):
+                if path == "default":
+                    os.environ.pop("W4A16_GEMV_PATH", None)
+                else:
+                    os.environ["W4A16_GEMV_PATH"] = path
+                kern = gemv_kernel_name(m, n, k)
+                if path == "valu" and not kern.startswith(("k_gemv_vchunk", "k_gemv_valu")):
+                    rec[path] = None  # no VALU kernel at this M
+                    continue
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):  # the path is chosen while capturing
+                    h = torch.cuda.current_stream().cuda_stream
+                    for i in range(64):
+                        launch(i, h)
+                for _ in range(2):
+                    g.replay()
+                graphs[path] = (g, kern)
+            torch.cuda.synchronize()
+            # the paths' graphs take turns, 3 rounds of 5 replays each
+            us = {path: [] for path in graphs}
+            for _ in range(3):
+                for path, (g, _) in graphs.items():
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(5):
+                        g.replay()
+                    b.record()
+                    torch.cuda.synchronize()
+                    us[path].append(a.elapsed_time(b) * 1e3 / (5 * 64))
+            for path, (g, kern) in graphs.items():
+                rec[path] = {"kernel": kern, "us": round(sorted(us[path])[1], 3)}
+            del graphs
+            os.environ.pop("W4A16_GEMV_PATH", None)
+            times = [rec[p]["us"] for p in ("valu", "mfma") if rec[p]]
+            rec["default_is_fastest_path"] = rec["default"]["us"] <= min(times) * 1.02
+            best_default += rec["default_is_fastest_path"]
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+        del ws, ss
+        torch.cuda.empty_cache()
+    print(json.dumps({"shapes": len(rows), "default_within_2pct_of_fastest_path": best_default}), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -198,6 +309,7 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--dispatch-table", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
@@ -205,6 +317,8 @@ def main() -> int:
         return 2
     if args.ingest_counters:
         return ingest_counters(*args.ingest_counters)
+    if args.dispatch_table:
+        return dispatch_table()
 
     import torch
 
@@ -291,28 +405,7 @@ def main() -> int:
 
     # ---------------------------------------------------------------- per call
     def time_graph(launch_i, n_launch: int) -> float:
-        """µs per launch of a graph of n_launch launches, HIP events on the
-        replay stream: the median of 3 rounds of 5 replays, after 2 untimed
-        replays (the first replays of a new graph run measurably slower)."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            h = torch.cuda.current_stream().cuda_stream
-            for i in range(n_launch):
-                launch_i(i, h)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        reps, rounds = 5, []
-        for _ in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            rounds.append(a.elapsed_time(b) * 1e3 / (reps * n_launch))
-        del g
-        return sorted(rounds)[1]
+        return graph_us_per_launch(torch, cap, launch_i, n_launch)
 
     per_call = []
     L = args.per_call_launches
