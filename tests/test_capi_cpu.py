@@ -182,13 +182,14 @@ def test_gemv_kernel_name_query(monkeypatch):
     # the MFMA kernels are named by the token rows they stage per step
     for m, xt in ((3, 4), (4, 4), (5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
-    for m, xt in ((5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
+    for m, xt in ((9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 6144, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
-    # up to 4 tokens where 24-row units fit the compute units and 16-row tiles do not
+    # up to 8 tokens where 24-row units fit the compute units and 16-row tiles do not
     # (the host-only query assumes 256 compute units when no GPU is present)
-    for m in (3, 4):
-        assert gemv_kernel_name(m, 6144, 4096) == "k_gemv_mfma_bd<false, 6>"
-    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 6>"
+    for m, tk in ((3, 4), (4, 4), (5, 8), (8, 8)):
+        assert gemv_kernel_name(m, 6144, 4096) == f"k_gemv_mfma_bd<false, {tk}>"
+    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 4>"
+    assert gemv_kernel_name(8, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8>"
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
     # BF16 at one token: MFMA up to K = 8192, the VALU kernel beyond

@@ -207,13 +207,14 @@ def test_nvfp4_dequant_gemm_strided_x_and_reuse():
     np.testing.assert_array_equal(a, b)  # the sums do not depend on timing (no atomics)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("n,k,silu", [(4112, 128, False), (4176, 320, False), (6144, 1024, False), (8448, 128, True),
                                       (8256, 64, True)])
 def test_nvfp4_gemv_24_row_units(m, n, k, silu, monkeypatch):
-    """Up to 4 tokens with more 16-row tiles than compute units but at most
-    one 24-row unit per compute unit: the block-diagonal MFMA kernel, with
-    ragged last units, partial 512-k super-steps and silu_mul."""
+    """Up to 8 tokens with more 16-row tiles than compute units but at most
+    one 24-row unit per compute unit: the block-diagonal MFMA kernels (4- and
+    8-token forms), with ragged last units, partial super-steps and
+    silu_mul."""
     _say("nvfp4_gemv 24-row units", m, n, k, silu)
     monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")  # also at 1 and 2 tokens
     assert lib.gemv_kernel_name(m, n, k, silu_mul=silu).startswith("k_gemv_mfma_bd<")

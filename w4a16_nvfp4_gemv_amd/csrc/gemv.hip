@@ -662,41 +662,49 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
   }
 }
 
-// ------------------------------------------------------------------ MFMA, block-diagonal (NVFP4, M <= 4)
+// ------------------------------------------------------------------ MFMA, block-diagonal (NVFP4, M <= 8)
 // For row counts whose 16-row tiles outnumber the compute units without
-// filling a second round (e.g. 6144 rows: 384 tiles on 256 units, half of
-// the units doing two), this form gives each workgroup G4 groups of 4
-// consecutive rows (24 rows for G4 = 6: 6144 rows are 256 workgroups).
-// With at most 4 tokens, 12 of the 16 B columns of the swap-AB MFMA would
-// carry copies; here they carry the K split instead:
+// filling a second round (e.g. 6144 rows: 384 tiles on 256 units, where half
+// the units did two tiles or, with two tiles per workgroup, a quarter of the
+// units idled), this form gives each workgroup 24 consecutive rows (6144
+// rows: 256 workgroups, one per unit).
+// With TK <= 8 tokens, the swap-AB MFMA's 16 B columns would carry 16 - TK
+// copies; here they carry a K split into KC = 16 / TK chunks instead:
 //
-//   A row    i = 4 rho + c   row rho (0..3) of a 4-row group, k chunk c (0..3)
-//   B column j = 4 n + c'    token n (0..3), k chunk c'
+//   A row    i = KC rho + c   row rho (0..TK-1) of a TK-row group, k chunk c
+//   B column j = KC n + c'    token n (0..TK-1), k chunk c'
 //
 // Lane (i, g) loads the 32 codes k = S + 128c + 32g .. +31 of its row (S =
-// first k of a 512-k super-step), so the 16 lanes of a row read its 256
-// bytes of the super-step in one load; MFMA f (0..3) takes fragment f of
-// those codes, k = S + 128c + 32g + 8f .. +7, against token n's
-// k = S + 128c' + 32g + 8f .. +7.  The products with c = c' (the diagonal 4x4
-// blocks) are the wanted ones; lane (col, g') of the C fragment holds rows
-// i = 4g' + q, so its diagonal entry is component q = col & 3, and the four
-// lanes col & 3 = 0..3 add theirs into out[n][row g' of the group].
-// The activations (4 tokens x 1 KB per super-step) arrive by 4 loads
-// straight into an LDS ring, token n's chunk ch at position
-// ch ^ ((4n + ch/16) & 15), so the 16 lanes of one B-fragment read hit 16
-// distinct bank groups.  The 4 waves split K and meet in LDS.
+// first k of a super-step of 128 KC k), so the 4 KC lanes of a row read
+// 64 KC contiguous bytes (256 for 4 tokens, 128 for 8) in one load; MFMA f
+// (0..3) takes fragment f of those codes, k = S + 128c + 32g + 8f .. +7,
+// against token n's k = S + 128c' + 32g + 8f .. +7.  The products with c = c'
+// (the diagonal blocks) are the wanted ones.  Lane (col, g') of the C
+// fragment holds rows i = 4g' + q; its diagonal entries are q = c' + KC u
+// (u < 4 / KC), i.e. group rows 4g' / KC + u, and the KC lanes col % KC add
+// theirs over the k chunks.  The activations (4 KB per super-step: TK
+// tokens x 128 KC k) arrive by 4 loads straight into an LDS ring, token n's
+// chunk ch at position ch ^ ((KC n + ch / 16) & 15), so the 16 lanes of one
+// B-fragment read hit 16 distinct bank groups.  The 4 waves split K and meet
+// in LDS.
 constexpr int kBdWaves = 4;
+constexpr int kBdRows = 24;            // rows per workgroup
 
-__device__ __forceinline__ int bd_pos(int n, int ch) { return ch ^ ((4 * n + (ch >> 4)) & 15); }
+template <int KC>
+__device__ __forceinline__ int bd_pos(int n, int ch) { return ch ^ ((KC * n + (ch >> 4)) & 15); }
 
-template <bool SILU, int G4>
+template <bool SILU, int TK>
 __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams p) {
+  static_assert(TK == 4 || TK == 8, "4 or 8 tokens");
+  constexpr int KC = 16 / TK;          // k chunks of the K split
+  constexpr int G = kBdRows / TK;      // TK-row groups per workgroup
   constexpr int W = kBdWaves;
   constexpr int D = 2;                 // super-steps in flight per wave
-  constexpr int NG = SILU ? 2 * G4 : G4;  // 4-row groups per unit (gate, then up)
-  constexpr int SSK = 512;             // k per super-step
-  constexpr int SLOT = 4 * 64;         // ring chunks (16 B) per wave and super-step
-  constexpr int LX = 4;                // staging loads per super-step (one token each)
+  constexpr int NG = SILU ? 2 * G : G; // groups (gate, then up)
+  constexpr int SSK = 128 * KC;        // k per super-step
+  constexpr int SEG = 16 * KC;         // ring chunks (16 B) per token and super-step
+  constexpr int SLOT = TK * SEG;       // ring chunks per wave and super-step (256)
+  constexpr int LX = SLOT / 64;        // staging loads per super-step (4)
   constexpr int PER = 2;               // loads per group and super-step: scale word, codes
   constexpr int L = LX + NG * PER;
   constexpr int FULL_AFTER = NG * PER + (D - 1) * L;
@@ -706,8 +714,8 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
-  const int rho = (lane & 15) >> 2;    // A: row of the group; B: token n
-  const int c = lane & 3;              // A: k chunk c; B: k chunk c'
+  const int rho = (lane & 15) / KC;    // A: row of the group; B: token n
+  const int c = lane % KC;             // A: k chunk c; B: k chunk c'
   const int64_t limit = SILU ? p.half : p.N;
   const uint32_t row_bytes = p.K / 2;
   const int64_t ss_total = (p.K + SSK - 1) / SSK;
@@ -719,24 +727,26 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
   const float gs = *p.gs;
 
-  // staging load n: token n, the chunk whose ring position is this lane
+  // staging load q: ring positions 64 q + lane, i.e. token (64 q + lane) / SEG
+  // and the chunk stored at that position
   uint32_t sxo[LX], sch[LX];
 #pragma unroll
-  for (int n = 0; n < LX; ++n) {
-    sch[n] = static_cast<uint32_t>(bd_pos(n, lane));  // bd_pos is its own inverse
-    sxo[n] = n < p.M ? static_cast<uint32_t>(n) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
+  for (int q = 0; q < LX; ++q) {
+    const int n = (64 * q + lane) / SEG;
+    sch[q] = static_cast<uint32_t>(bd_pos<KC>(n, (64 * q + lane) % SEG));  // bd_pos is its own inverse
+    sxo[q] = n < p.M ? static_cast<uint32_t>(n) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
   }
 
   for (int64_t unit = xcd_logical_block(); unit < p.units; unit += gridDim.x) {
     int64_t rows[NG];
     bool rv[NG];
 #pragma unroll
-    for (int a = 0; a < G4; ++a) {
-      rows[a] = unit * (4 * G4) + 4 * a + rho;
+    for (int a = 0; a < G; ++a) {
+      rows[a] = unit * kBdRows + TK * a + rho;
       rv[a] = rows[a] < limit;
       if constexpr (SILU) {
-        rows[G4 + a] = rows[a] + p.half;
-        rv[G4 + a] = rv[a];
+        rows[G + a] = rows[a] + p.half;
+        rv[G + a] = rv[a];
       }
     }
     u32x4 wb[D][NG];
@@ -745,10 +755,10 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
       const bool sv = st < nst;
       const uint32_t kb = static_cast<uint32_t>((st0 + st) * SSK);
 #pragma unroll
-      for (int n = 0; n < LX; ++n) {
-        const uint32_t k = kb + sch[n] * 8;
-        bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + n * 64,
-                    off_if(sv && k < static_cast<uint32_t>(p.K), sxo[n] + k * 2));
+      for (int q = 0; q < LX; ++q) {
+        const uint32_t k = kb + sch[q] * 8;
+        bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + q * 64,
+                    off_if(sv && k < static_cast<uint32_t>(p.K), sxo[q] + k * 2));
       }
       // K % 64 == 0: the lane's 32 codes are all in range or all out
       const uint32_t k = kb + 128 * c + 32 * g;
@@ -773,7 +783,7 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
       vm_wait_n(after);
 #pragma unroll
       for (int f = 0; f < 4; ++f)
-        xf[f] = xl_slot<W * SLOT>(d)[wave * SLOT + rho * 64 + bd_pos(rho, 16 * c + 4 * g + f)];
+        xf[f] = xl_slot<W * SLOT>(d)[wave * SLOT + rho * SEG + bd_pos<KC>(rho, 16 * c + 4 * g + f)];
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -799,31 +809,38 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
     }
     __syncthreads();
     if (wave == 0) {
-      float v[NG];
+      constexpr int U = 4 / KC;        // diagonal entries per lane
+      float v[NG][U];
 #pragma unroll
       for (int a = 0; a < NG; ++a) {
 #pragma unroll
         for (int w = 0; w < W - 1; ++w) acc[a] += red[w][a][lane];
-        // the diagonal entry (c == c'), then the sum over the four k chunks
-        float e = c == 0 ? acc[a][0] : c == 1 ? acc[a][1] : c == 2 ? acc[a][2] : acc[a][3];
-        e += __shfl_xor(e, 1);
-        e += __shfl_xor(e, 2);
-        v[a] = e;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // component q = c' + KC u (c == c'), then the sum over the KC k chunks
+          const int q = c + KC * u;
+          float e = q == 0 ? acc[a][0] : q == 1 ? acc[a][1] : q == 2 ? acc[a][2] : acc[a][3];
+#pragma unroll
+          for (int sh = 1; sh < KC; sh <<= 1) e += __shfl_xor(e, sh);
+          v[a][u] = e;
+        }
       }
-      const int n = rho;               // C column 4n + c'
+      const int n = rho;               // C column KC n + c'
       if (c == 0 && n < p.M) {
 #pragma unroll
-        for (int a = 0; a < G4; ++a) {
-          const int64_t row = unit * (4 * G4) + 4 * a + g;  // C rows 4g' + q: group row g'
-          if (row >= limit) continue;
-          if constexpr (!SILU) {
-            p.out[n * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[a] * gs);
-          } else {
-            const float gv = bf16_bits_to_f32(f32_to_bf16_bits(v[a] * gs));
-            const float uv = bf16_bits_to_f32(f32_to_bf16_bits(v[G4 + a] * gs));
-            p.out[n * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+        for (int a = 0; a < G; ++a)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t row = unit * kBdRows + TK * a + (4 / KC) * g + u;  // C rows 4g' + q
+            if (row >= limit) continue;
+            if constexpr (!SILU) {
+              p.out[n * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[a][u] * gs);
+            } else {
+              const float gv = bf16_bits_to_f32(f32_to_bf16_bits(v[a][u] * gs));
+              const float uv = bf16_bits_to_f32(f32_to_bf16_bits(v[G + a][u] * gs));
+              p.out[n * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+            }
           }
-        }
       }
     }
     __syncthreads();
@@ -960,23 +977,22 @@ int device_cu_count() {
   return n;
 }
 
-// The block-diagonal form with 24-row units where the 16-row tiles outnumber
-// the compute units but the 24-row units do not (measured at 6144 rows).
-template <bool SILU>
+// The block-diagonal form (24-row units) where the 16-row tiles outnumber the
+// compute units but the 24-row units do not (measured at 6144 rows).
+template <bool SILU, int TK>
 bool launch_mfma_bd24(GemvParams p, hipStream_t stream, hipError_t* err) {
-  constexpr int G4 = 6;
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles16 = (limit + 15) / 16;
-  const int64_t units = (limit + 4 * G4 - 1) / (4 * G4);
+  const int64_t units = (limit + kBdRows - 1) / kBdRows;
   const int cus = device_cu_count();
   if (!(tiles16 > cus && units <= cus)) return false;
   p.units = units;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma_bd<%s, %d>", tf(SILU), G4);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma_bd<%s, %d>", tf(SILU), TK);
     *err = hipSuccess;
     return true;
   }
-  hipLaunchKernelGGL((k_gemv_mfma_bd<SILU, G4>), dim3(static_cast<unsigned>(units)), dim3(kBdWaves * 64), 0, stream,
+  hipLaunchKernelGGL((k_gemv_mfma_bd<SILU, TK>), dim3(static_cast<unsigned>(units)), dim3(kBdWaves * 64), 0, stream,
                      p);
   *err = hipGetLastError();
   return true;
@@ -1021,7 +1037,8 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   p.tiles = p.K / 64;
   if constexpr (FP4) {
     hipError_t err;
-    if (p.M <= 4 && launch_mfma_bd24<SILU>(p, stream, &err)) return err;
+    if (p.M <= 4 && launch_mfma_bd24<SILU, 4>(p, stream, &err)) return err;
+    if (p.M > 4 && p.M <= 8 && launch_mfma_bd24<SILU, 8>(p, stream, &err)) return err;
   }
   if (p.M <= 4) return launch_mfma<FP4, 4, SILU>(p, stream);
   if (p.M <= 8) return launch_mfma<FP4, 8, SILU>(p, stream);
