@@ -227,6 +227,19 @@ def test_nvfp4_gemv_24_row_units(m, n, k, silu, monkeypatch):
         check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [3, 8])
+def test_nvfp4_gemv_24_row_units_long_rows(m):
+    """The block-diagonal kernels over many super-steps per wave (K = 16448:
+    the ring refills, ragged last super-step)."""
+    n, k = 4176, 16448
+    _say("nvfp4_gemv 24-row units long", m, n, k)
+    assert lib.gemv_kernel_name(m, n, k).startswith("k_gemv_mfma_bd<")
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 11)
+    got = run_nvfp4(d, n)
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("m", [8, 17, 32])
 @pytest.mark.parametrize("n,k,silu", [(4224, 128, False), (4176, 192, False), (8448, 128, True), (8256, 64, True)])
 def test_nvfp4_gemv_many_row_tiles(m, n, k, silu):
