@@ -187,9 +187,12 @@ def test_gemv_kernel_name_query(monkeypatch):
     # up to 8 tokens where 24-row units fit the compute units and 16-row tiles do not
     # (the host-only query assumes 256 compute units when no GPU is present)
     for m, tk in ((3, 4), (4, 4), (5, 8), (8, 8)):
-        assert gemv_kernel_name(m, 6144, 4096) == f"k_gemv_mfma_bd<false, {tk}>"
-    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 4>"
-    assert gemv_kernel_name(8, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8>"
+        assert gemv_kernel_name(m, 6144, 4096) == f"k_gemv_mfma_bd<false, {tk}, 24>"
+    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 4, 24>"
+    assert gemv_kernel_name(8, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 24>"
+    # 5..8 tokens where only 56-row units fit (the fused silu call on 2 x 14336 rows)
+    assert gemv_kernel_name(8, 28672, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 56>"
+    assert gemv_kernel_name(4, 28672, 4096, silu_mul=True).startswith("k_gemv_mfma<true, 4, true,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
     # BF16 at one token: MFMA up to K = 8192, the VALU kernel beyond

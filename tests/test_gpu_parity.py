@@ -227,6 +227,22 @@ def test_nvfp4_gemv_24_row_units(m, n, k, silu, monkeypatch):
         check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [5, 7, 8])
+@pytest.mark.parametrize("n,k,silu", [(14336, 256, False), (14000, 192, False), (28672, 128, True)])
+def test_nvfp4_gemv_56_row_units(m, n, k, silu):
+    """5..8 tokens where only 56-row units fit the compute units (14336 rows
+    and the fused silu call on 2 x 14336), including a ragged last unit."""
+    _say("nvfp4_gemv 56-row units", m, n, k, silu)
+    assert lib.gemv_kernel_name(m, n, k, silu_mul=silu) == f"k_gemv_mfma_bd<{'true' if silu else 'false'}, 8, 56>"
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k + 13)
+    got = run_nvfp4(d, n, silu=silu)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, d["gs"][0], f"silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("m", [3, 8])
 def test_nvfp4_gemv_24_row_units_long_rows(m):
     """The block-diagonal kernels over many super-steps per wave (K = 16448:

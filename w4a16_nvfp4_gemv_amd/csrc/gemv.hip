@@ -688,16 +688,16 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
 // B-fragment read hit 16 distinct bank groups.  The 4 waves split K and meet
 // in LDS.
 constexpr int kBdWaves = 4;
-constexpr int kBdRows = 24;            // rows per workgroup
 
 template <int KC>
 __device__ __forceinline__ int bd_pos(int n, int ch) { return ch ^ ((KC * n + (ch >> 4)) & 15); }
 
-template <bool SILU, int TK>
+template <bool SILU, int TK, int R>
 __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams p) {
   static_assert(TK == 4 || TK == 8, "4 or 8 tokens");
+  static_assert(R % TK == 0, "whole groups per workgroup");
   constexpr int KC = 16 / TK;          // k chunks of the K split
-  constexpr int G = kBdRows / TK;      // TK-row groups per workgroup
+  constexpr int G = R / TK;            // TK-row groups per workgroup (R rows)
   constexpr int W = kBdWaves;
   constexpr int D = 2;                 // super-steps in flight per wave
   constexpr int NG = SILU ? 2 * G : G; // groups (gate, then up)
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
     bool rv[NG];
 #pragma unroll
     for (int a = 0; a < G; ++a) {
-      rows[a] = unit * kBdRows + TK * a + rho;
+      rows[a] = unit * R + TK * a + rho;
       rv[a] = rows[a] < limit;
       if constexpr (SILU) {
         rows[G + a] = rows[a] + p.half;
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
         for (int a = 0; a < G; ++a)
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int64_t row = unit * kBdRows + TK * a + (4 / KC) * g + u;  // C rows 4g' + q
+            const int64_t row = unit * R + TK * a + (4 / KC) * g + u;  // C rows 4g' + q
             if (row >= limit) continue;
             if constexpr (!SILU) {
               p.out[n * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[a][u] * gs);
@@ -977,23 +977,25 @@ int device_cu_count() {
   return n;
 }
 
-// The block-diagonal form (24-row units) where the 16-row tiles outnumber the
-// compute units but the 24-row units do not (measured at 6144 rows).
-template <bool SILU, int TK>
-bool launch_mfma_bd24(GemvParams p, hipStream_t stream, hipError_t* err) {
+// The block-diagonal form with R-row units where the 16-row tiles outnumber
+// the compute units but the R-row units do not (measured: 24 rows at 6144
+// rows for 1..8 tokens; 56 rows at 14336 rows for 5..8 tokens, where at 4
+// tokens it was slower than the 16-row tiles).
+template <bool SILU, int TK, int R>
+bool launch_mfma_bd(GemvParams p, hipStream_t stream, hipError_t* err) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles16 = (limit + 15) / 16;
-  const int64_t units = (limit + kBdRows - 1) / kBdRows;
+  const int64_t units = (limit + R - 1) / R;
   const int cus = device_cu_count();
   if (!(tiles16 > cus && units <= cus)) return false;
   p.units = units;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma_bd<%s, %d>", tf(SILU), TK);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma_bd<%s, %d, %d>", tf(SILU), TK, R);
     *err = hipSuccess;
     return true;
   }
-  hipLaunchKernelGGL((k_gemv_mfma_bd<SILU, TK>), dim3(static_cast<unsigned>(units)), dim3(kBdWaves * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((k_gemv_mfma_bd<SILU, TK, R>), dim3(static_cast<unsigned>(units)), dim3(kBdWaves * 64), 0,
+                     stream, p);
   *err = hipGetLastError();
   return true;
 }
@@ -1037,8 +1039,9 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   p.tiles = p.K / 64;
   if constexpr (FP4) {
     hipError_t err;
-    if (p.M <= 4 && launch_mfma_bd24<SILU, 4>(p, stream, &err)) return err;
-    if (p.M > 4 && p.M <= 8 && launch_mfma_bd24<SILU, 8>(p, stream, &err)) return err;
+    if (p.M <= 4 && launch_mfma_bd<SILU, 4, 24>(p, stream, &err)) return err;
+    if (p.M > 4 && p.M <= 8 && launch_mfma_bd<SILU, 8, 24>(p, stream, &err)) return err;
+    if (p.M > 4 && p.M <= 8 && launch_mfma_bd<SILU, 8, 56>(p, stream, &err)) return err;
   }
   if (p.M <= 4) return launch_mfma<FP4, 4, SILU>(p, stream);
   if (p.M <= 8) return launch_mfma<FP4, 8, SILU>(p, stream);
