@@ -287,11 +287,15 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const GemvParams p) {
 // chunk by chunk), the 8 products of a chunk are summed in FP32 and scaled
 // once, each wave's partial sums meet through a permlane reduce-scatter, and
 // the KS slices are added in slice order through LDS.
-template <int MT, bool SILU, int C, int KS>
+// PAIR (without silu_mul): a unit is two adjacent quads (rows r and r + 1 of
+// each quad position), so every activation chunk a wave loads serves 8 rows
+// instead of 4 and the two quads' scale chunks share one cache line.
+template <int MT, bool SILU, int C, int KS, bool PAIR>
 __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
-  constexpr int R = SILU ? 8 : 4;
+  static_assert(!(SILU && PAIR), "a pair unit has no up half");
+  constexpr int R = (SILU || PAIR) ? 8 : 4;
   constexpr int NQ = R / 4;
-  constexpr int P = SILU ? 2 : 1;
+  constexpr int P = (SILU || PAIR) ? 2 : 1;
   constexpr int V = MT * 4 * P;  // value index v = (m * 4 + q) * P + u
   using RS = ReduceScatter<V, P>;
   const int tid = threadIdx.x;
@@ -308,7 +312,17 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
   const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
 
   const float gs = *p.gs;
-  const UnitRows<R> ur = unit_rows<true, SILU, R>(p, unit);
+  UnitRows<R> ur;
+  if constexpr (PAIR) {
+    // quads 2 unit and 2 unit + 1: the second quad's rows are the first's + 1
+    quad_rows<R>(2 * static_cast<int64_t>(unit), p.N, 1, ur.rows, ur.rv);
+#pragma unroll
+    for (int i = 0; i < R; ++i) ur.rv[i] = ur.rv[i] && unit < p.units;
+    ur.quad_ok[0] = true;
+    ur.quad_ok[1] = true;
+  } else {
+    ur = unit_rows<true, SILU, R>(p, unit);
+  }
 
   u32x4 xv[MT][C];
 #pragma unroll
@@ -409,9 +423,14 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
   for (int j = 0; j < RS::LEFT / P; ++j) {
     const int vi = base + j * P;
     const int m = vi / (4 * P), q = (vi / P) % 4;
-    const int64_t row = (static_cast<int64_t>(unit) >> 5) * 128 + (unit & 31) + 32 * q;
+    const int64_t qu = PAIR ? 2 * static_cast<int64_t>(unit) : unit;  // (first) quad of the unit
+    const int64_t row = (qu >> 5) * 128 + (qu & 31) + 32 * q;
     if (kw == 0 && (lane & 15) == j && m < p.M && unit < p.units && row < limit) {
-      if constexpr (!SILU) {
+      if constexpr (PAIR) {
+        // N % 16 == 0: row r < N (r even) implies r + 1 < N
+        p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[j * P] * gs);
+        p.out[m * static_cast<int64_t>(p.N) + row + 1] = f32_to_bf16_bits(v[j * P + 1] * gs);
+      } else if constexpr (!SILU) {
         p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(v[j] * gs);
       } else {
         const float g = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P] * gs));
@@ -886,15 +905,21 @@ hipError_t launch_valu_lpq(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Pair units (two adjacent quads) for one or two tokens without silu_mul
+// (measured: 4096 x 4096 at 1 / 2 tokens 4.41 / 5.08 -> 4.17 / 4.80 us).
+constexpr bool kVchunkPairs = true;
+
 template <int MT, bool SILU, int C, int KS>
-hipError_t launch_vchunk_c(const GemvParams& p, hipStream_t stream) {
+hipError_t launch_vchunk_c(GemvParams p, hipStream_t stream) {
   constexpr int upb = 4 / KS;
+  constexpr bool PAIR = kVchunkPairs && !SILU && MT <= 2;
+  if constexpr (PAIR) p.units = (p.units + 1) / 2;  // quads come 32 to a band, so this is exact
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_vchunk<%d, %s, %d, %d>", MT, tf(SILU), C, KS);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_vchunk<%d, %s, %d, %d, %s>", MT, tf(SILU), C, KS, tf(PAIR));
     return hipSuccess;
   }
   const dim3 grid(static_cast<unsigned>((p.units + upb - 1) / upb)), block(256);
-  hipLaunchKernelGGL((k_gemv_vchunk<MT, SILU, C, KS>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((k_gemv_vchunk<MT, SILU, C, KS, PAIR>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
