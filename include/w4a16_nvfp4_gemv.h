@@ -32,10 +32,13 @@
  * Shape limits shared by the GEMV entry points: 0 <= M <= 64 tokens (M == 0
  * is a successful no-op; the pages' kernels stop at 32 tokens, the MFMA
  * kernels here take up to four 16-token tiles), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
- * Pointer alignment: activations, weights and scale buffers 16 bytes,
- * global scale 4 bytes, outputs 2 bytes; the row stride ldx of x is a
- * multiple of 8 elements.  Each of x, the weight and the scale buffer must
- * span less than 2 GiB.
+ * Pointer alignment: activations and weights 16 bytes, scale buffers and
+ * global scales 4 bytes (one 32-bit word holds a row's 4 scales of a 64-k
+ * tile: the 4-byte divisibility of the moe_gemv page's fake tensor specs),
+ * outputs 2 bytes; the row stride ldx of x is a multiple of 8 elements.  A
+ * scale buffer that is 4- but not 16-byte aligned is served by the kernels
+ * that read one scale word per row (the MFMA forms), with the same results.
+ * Each of x, the weight and the scale buffer must span less than 2 GiB.
  *
  * The kernels read past-the-end rows and tiles through buffer resources that
  * return zeros, so no entry point reads outside the extents given here; the
@@ -191,7 +194,9 @@ int moe_down_combine(const uint16_t *act, const int32_t *ids, const float *tw, i
  */
 const char *w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage).  The two names are
+ * the same function. */
+const char *nvfp4_status_string(int status);
 const char *w4a16_status_string(int status);
 
 /* Detail of the last failed call on this host thread (static per-thread

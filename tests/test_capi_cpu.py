@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["nvfp4_gemv", "bf16_gemv", "dequantize_rows", "moe_gate_up", "moe_down_combine",
                  "nvfp4_unswizzle_scales", "nvfp4_dequant_gemm", "nvfp4_dequant_gemm_workspace_bytes",
-                 "w4a16_status_string", "w4a16_last_error"]:
+                 "nvfp4_status_string", "w4a16_status_string", "w4a16_last_error"]:
         assert want in names
 
 
@@ -46,6 +46,8 @@ def test_status_strings():
     lib = _lib.load()
     assert lib.w4a16_status_string(OK) == b"ok"
     assert lib.w4a16_status_string(UNSUPPORTED) == b"unsupported shape"
+    for st in range(-1, 6):  # the boundary's name and the library's name are one function
+        assert lib.nvfp4_status_string(st) == lib.w4a16_status_string(st)
 
 
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: calls fail validation first
@@ -71,7 +73,8 @@ def gemv(**kw):
     (dict(ldx=4100), MISALIGNED),        # ldx % 8 != 0
     (dict(x=FAKE + 2), MISALIGNED),
     (dict(w=FAKE + 8), MISALIGNED),
-    (dict(s=FAKE + 4), MISALIGNED),
+    (dict(s=FAKE + 2), MISALIGNED),      # scales need 4-byte alignment (4-byte views run on the GPU tests)
+    (dict(s=FAKE + 1), MISALIGNED),
     (dict(gs=FAKE + 2), MISALIGNED),
     (dict(out=FAKE + 1), MISALIGNED),
     (dict(x=None), INVALID),
@@ -159,6 +162,8 @@ def test_moe_argument_errors():
     assert gu(I=1544 - 1) == UNSUPPORTED
     assert gu(ids=None) == INVALID
     assert gu(w1=FAKE + 4) == MISALIGNED
+    assert gu(s1=FAKE + 2) == MISALIGNED
+    assert gu(ssh=FAKE + 1) == MISALIGNED
     assert gu(M=0, x=None, ids=None) == OK
     dc = lambda **kw: lib.moe_down_combine(*[kw.get(k, v) for k, v in dict(
         act=FAKE, ids=FAKE, tw=FAKE, M=1, topk=8, E=128, w2=FAKE, s2=FAKE, alpha2=FAKE, H=4096,
@@ -168,6 +173,8 @@ def test_moe_argument_errors():
     assert dc(H=4104) == UNSUPPORTED   # H % 16
     assert dc(tw=None) == INVALID
     assert dc(act=FAKE + 8) == MISALIGNED
+    assert dc(s2=FAKE + 2) == MISALIGNED
+    assert dc(ssd=FAKE + 2) == MISALIGNED
     assert dc(M=0, act=None) == OK
 
 

@@ -321,6 +321,62 @@ def test_nvfp4_gemv_row_stride_and_zero_tokens():
     assert tuple(empty.shape) == (0, n)
 
 
+def at_offset(t, off):
+    """A device copy of `t` whose data pointer is `off` bytes past a 256-byte
+    boundary (a 4- but not 16-byte aligned view for off = 4)."""
+    raw = t.contiguous().view(torch.uint8).reshape(-1)
+    buf = torch.zeros(raw.numel() + 512, dtype=torch.uint8, device=DEV)
+    start = (-buf.data_ptr()) % 256 + off
+    view = buf[start:start + raw.numel()]
+    view.copy_(dev(raw))
+    assert view.data_ptr() % 256 == off
+    return view.view(t.dtype).reshape(t.shape)
+
+
+@pytest.mark.parametrize("off", [4, 8, 12])
+@pytest.mark.parametrize("m,n,k,silu", [(1, 256, 512, False), (2, 272, 1088, False), (1, 512, 1024, True),
+                                        (3, 256, 512, False), (8, 6144, 256, False), (32, 512, 1024, True),
+                                        (2, 64, 20480, False)])
+def test_nvfp4_gemv_scale_buffer_4_byte_aligned(m, n, k, silu, off):
+    """Scale buffers need only 4-byte alignment (a row's 4 scales of a 64-k
+    tile are one 32-bit word): a view 4, 8 or 12 bytes past a 16-byte
+    boundary gives results within the bound at token counts and shapes of
+    every kernel family (the calls whose default kernel reads 16-byte scale
+    chunks run the MFMA kernels)."""
+    _say("nvfp4_gemv 4-byte scales", m, n, k, silu, off)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + n + k + off)
+    s_view = at_offset(d["s"], off)
+    out = to_bits(lib.nvfp4_gemv(dev(d["x"]), dev(d["w"]), s_view, dev(d["gs"]), silu_mul=silu).cpu())
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(out, want, acc, absacc, d["gs"][0], f"4-byte scales silu M={m} N={n} K={k}")
+    else:
+        check_gemv(out, acc, absacc, d["gs"][0], k, f"4-byte scales M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 5])
+def test_moe_scale_buffers_4_byte_aligned(m):
+    """The MoE pair with every scale buffer 4 bytes past a 16-byte boundary
+    (one and two tokens then run the MFMA forms)."""
+    e, topk, h, inter, si = 6, 3, 256, 128, 192
+    wts = synth.moe_weights(e, h, inter, si, seed=500 + m)
+    tok = synth.moe_tokens(m, h, e, topk, seed=510 + m)
+    _say("moe 4-byte scales", m)
+    gw = {k: dev(v) for k, v in wts.items()}
+    for name in ("w1_sf", "ssh", "w2_sf", "ssd"):
+        gw[name] = at_offset(wts[name], 4)
+    act = torch.empty((m * topk, inter), dtype=torch.bfloat16, device=DEV)
+    sact = torch.empty((m, si), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((m, h), dtype=torch.bfloat16, device=DEV)
+    ids = dev(tok["ids"])
+    lib.moe_gate_up(dev(tok["x"]), ids, gw["w1"], gw["w1_sf"], gw["alpha"], act, gw["wsh"], gw["ssh"], gw["gssh"],
+                    sact)
+    lib.moe_down_combine(act, ids, dev(tok["tw"]), gw["w2"], gw["w2_sf"], gw["alpha2"], sact, gw["wsd"], gw["ssd"],
+                         gw["gssd"], out)
+    torch.cuda.synchronize()
+    moe_check(wts, tok, act.cpu(), sact.cpu(), to_bits(out.cpu()), list(range(m)), f"moe 4-byte scales M={m}")
+
+
 @pytest.mark.parametrize("m", [1, 2, 5, 17, 40])
 def test_gemv_row_strided_activations_every_family(m):
     """x with a row stride past K (ldx = K + 64) on each kernel family: the

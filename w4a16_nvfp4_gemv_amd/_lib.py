@@ -25,6 +25,7 @@ SIGNATURES = {
     "moe_gate_up": (_int, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "moe_down_combine": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "w4a16_gemv_kernel_name": (ctypes.c_char_p, [_int, _i64, _i64, _i64, _int]),
+    "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_last_error": (ctypes.c_char_p, []),
 }

@@ -72,6 +72,8 @@ const char* w4a16_status_string(int status) {
   }
 }
 
+const char* nvfp4_status_string(int status) { return w4a16_status_string(status); }
+
 const char* w4a16_last_error(void) { return g_last_error.c_str(); }
 
 int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
@@ -80,7 +82,7 @@ int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8
   int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 64);
   if (st != W4A16_OK || M == 0) return st;
   if (!w_scale || !global_scale) return fail(W4A16_ERR_INVALID_ARG, "null scale pointer");
-  if (!aligned(w_scale, 16) || !aligned(global_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w_scale must be 16-byte aligned");
+  if (!aligned(w_scale, 4) || !aligned(global_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w_scale and global_scale must be 4-byte aligned");
   const int64_t w_bytes = N * (K / 2), s_bytes = flat_scale_bytes(N, K), x_bytes = ((M - 1) * ldx + K) * 2;
   if (w_bytes > kMaxDim || s_bytes > kMaxDim || x_bytes > kMaxDim)
     return fail(W4A16_ERR_UNSUPPORTED, "tensors above 2 GiB are not supported (weight %lld bytes)", w_bytes);
@@ -98,7 +100,10 @@ int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8
   p.N = static_cast<int>(N);
   p.K = static_cast<int>(K);
   p.half = silu_mul ? static_cast<int>(N / 2) : 0;
-  const int path = w4a16::choose_gemv_path(true, M, N, K);
+  // The VALU kernels read a quad's scale words as one 16-byte chunk; a scale
+  // buffer that is only 4-byte aligned goes to the MFMA kernels, which read
+  // one 4-byte word per row.
+  const int path = aligned(w_scale, 16) ? w4a16::choose_gemv_path(true, M, N, K) : w4a16::kPathMfma;
   return hip_status(w4a16::launch_gemv(true, p, silu_mul, path, static_cast<hipStream_t>(stream)));
 }
 
@@ -222,8 +227,8 @@ int moe_gate_up(const uint16_t* x, int64_t M, int64_t H, const int32_t* ids, int
   if (H > kMaxDim || I > kMaxDim / 2 || SI > kMaxDim / 2 || E > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "size too large");
   if (M == 0) return ok();
   if (!x || !ids || !w1 || !w1_scale || !alpha || !act || !wsh || !ssh || !gssh || !sact) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
-  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w1_scale, 16) || !aligned(wsh, 16) || !aligned(ssh, 16))
-    return fail(W4A16_ERR_MISALIGNED, "x, weights and scales must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(wsh, 16) || !aligned(w1_scale, 4) || !aligned(ssh, 4))
+    return fail(W4A16_ERR_MISALIGNED, "x and weights must be 16-byte aligned, scales 4-byte aligned");
   if (!aligned(ids, 4) || !aligned(alpha, 4) || !aligned(gssh, 4) || !aligned(act, 2) || !aligned(sact, 2))
     return fail(W4A16_ERR_MISALIGNED, "misaligned ids/alpha/outputs");
   w4a16::MoeGateUpParams p{};
@@ -250,6 +255,7 @@ int moe_gate_up(const uint16_t* x, int64_t M, int64_t H, const int32_t* ids, int
   p.E = static_cast<int>(E);
   p.I = static_cast<int>(I);
   p.SI = static_cast<int>(SI);
+  p.scales16 = aligned(w1_scale, 16) && aligned(ssh, 16);
   return hip_status(w4a16::launch_moe_gate_up(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -265,8 +271,9 @@ int moe_down_combine(const uint16_t* act, const int32_t* ids, const float* tw, i
   if (M == 0) return ok();
   if (!act || !ids || !tw || !w2 || !w2_scale || !alpha2 || !sact || !wsd || !ssd || !gssd || !out)
     return fail(W4A16_ERR_INVALID_ARG, "null pointer");
-  if (!aligned(act, 16) || !aligned(sact, 16) || !aligned(w2, 16) || !aligned(w2_scale, 16) || !aligned(wsd, 16) || !aligned(ssd, 16))
-    return fail(W4A16_ERR_MISALIGNED, "activations, weights and scales must be 16-byte aligned");
+  if (!aligned(act, 16) || !aligned(sact, 16) || !aligned(w2, 16) || !aligned(wsd, 16) || !aligned(w2_scale, 4) ||
+      !aligned(ssd, 4))
+    return fail(W4A16_ERR_MISALIGNED, "activations and weights must be 16-byte aligned, scales 4-byte aligned");
   if (!aligned(ids, 4) || !aligned(tw, 4) || !aligned(alpha2, 4) || !aligned(gssd, 4) || !aligned(out, 2))
     return fail(W4A16_ERR_MISALIGNED, "misaligned ids/tw/alpha2/out");
   w4a16::MoeDownParams p{};
@@ -294,6 +301,7 @@ int moe_down_combine(const uint16_t* act, const int32_t* ids, const float* tw, i
   p.H = static_cast<int>(H);
   p.I = static_cast<int>(I);
   p.SI = static_cast<int>(SI);
+  p.scales16 = aligned(w2_scale, 16) && aligned(ssd, 16);
   return hip_status(w4a16::launch_moe_down_combine(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -56,6 +56,7 @@ struct MoeGateUpParams {
   int64_t w1_expert_bytes, s1_expert_bytes, wsh_bytes, ssh_bytes;
   int M, H, topk, E, I, SI;
   int slots_max;          // min(M * topk, E): workgroup rows of routed experts
+  bool scales16;          // both scale buffers 16-byte aligned (the VALU forms need it)
 };
 
 struct MoeDownParams {
@@ -72,6 +73,7 @@ struct MoeDownParams {
   uint16_t* out;          // [M][H]
   int64_t w2_expert_bytes, s2_expert_bytes, wsd_bytes, ssd_bytes;
   int M, topk, E, H, I, SI;
+  bool scales16;          // both scale buffers 16-byte aligned (the VALU forms need it)
 };
 
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream);

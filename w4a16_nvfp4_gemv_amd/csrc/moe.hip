@@ -942,7 +942,8 @@ int chunks_per_lane(int64_t k, int64_t lanes, int cmax) {
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   const int pairs = p.M * p.topk;
   p.slots_max = pairs < p.E ? pairs : p.E;
-  if (moe_use_mfma(p.M)) {
+  // (the VALU forms read a quad's scale words as one 16-byte chunk)
+  if (moe_use_mfma(p.M) || !p.scales16) {
     // one work unit per wave at least, two resident workgroups per CU at most
     const int64_t units = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 8) + (p.SI + 127) / 128 * 8;
     int64_t blocks = (units + kMoeGateUpWaves - 1) / kMoeGateUpWaves;
@@ -958,7 +959,7 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
 }
 
 hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
-  if (moe_use_mfma(p.M)) {
+  if (moe_use_mfma(p.M) || !p.scales16) {
     const int64_t tiles = (p.H + 127) / 128 * 8;
     const dim3 grid(static_cast<unsigned>(tiles < 4096 ? tiles : 4096)), block(kMoeDownWaves * 64);
     if (p.M <= 4) hipLaunchKernelGGL((k_moe_down_mfma<4>), grid, block, 0, stream, p);
