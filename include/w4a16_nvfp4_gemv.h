@@ -92,6 +92,43 @@ int bf16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
               const uint16_t *w, int64_t N, int silu_mul, uint16_t *out, void *stream);
 
 /*
+ * nvfp4_gemv_splitk, bf16_gemv_splitk -- the nvfp4_gemv and bf16_gemv
+ * results, with a workspace that lets the library split K across
+ * workgroups: the nvfp4_gemv page (module docstring) splits K across the
+ * warps of a CTA and, with split > 1, across the CTAs of a cluster, reducing
+ * through shared memory.  Here the workgroups of a unit of row tiles each
+ * sum a K range in FP32, write the partial sums to the workspace, and the
+ * last one to arrive adds them in split order (so the result does not depend
+ * on timing) and applies the same epilogue (global scale, single BF16
+ * rounding, silu_mul).  Used from 16 tokens on, where every workgroup would
+ * otherwise stream all M*K*2 activation bytes.
+ *   Arguments as nvfp4_gemv / bf16_gemv, plus:
+ *   workspace        device memory owned by the caller, 256-byte aligned, of
+ *                    at least gemv_splitk_workspace_bytes(...) bytes for these
+ *                    sizes.  Its first bytes are per-unit arrival counters:
+ *                    they must be ZERO before the first call (e.g. memset
+ *                    once after allocation); every call leaves them zero.
+ *                    Calls that share a workspace must not overlap.
+ *   workspace_bytes  its size.
+ * When the plan for these sizes uses no split (the size query returns 0),
+ * workspace may be NULL and the call is exactly nvfp4_gemv / bf16_gemv.
+ * Errors as nvfp4_gemv; a missing or too small workspace returns
+ * W4A16_ERR_INVALID_ARG, a workspace that is not 256-byte aligned
+ * W4A16_ERR_MISALIGNED.
+ * gemv_splitk_workspace_bytes(weight_fp4, ...) returns the bytes the call
+ * needs on the current device (the plan depends on its compute units), 0
+ * when it uses no split, and -1 for sizes the entry points reject.
+ */
+int64_t gemv_splitk_workspace_bytes(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul);
+int nvfp4_gemv_splitk(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                      const uint8_t *w, const uint8_t *w_scale, const float *global_scale,
+                      int64_t N, int silu_mul, void *workspace, int64_t workspace_bytes,
+                      uint16_t *out, void *stream);
+int bf16_gemv_splitk(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint16_t *w,
+                     int64_t N, int silu_mul, void *workspace, int64_t workspace_bytes,
+                     uint16_t *out, void *stream);
+
+/*
  * dequantize_rows -- out[rows][K] = bf16(e2m1 * e4m3), bit-exact, global
  * scale not applied (nvfp4_gemv page, function dequantize_rows).
  * Needs rows % 16 == 0 and K % 256 == 0 (the page's assertion).
@@ -188,11 +225,13 @@ int moe_down_combine(const uint16_t *act, const int32_t *ids, const float *tw, i
  * the kernel instantiation (as profilers print it, without the namespace and
  * parameter list) that nvfp4_gemv (weight_fp4 = 1) or bf16_gemv
  * (weight_fp4 = 0) launches for these sizes and silu_mul, under the current
- * W4A16_GEMV_PATH setting.  Returns "" and records the reason in
+ * W4A16_GEMV_PATH and W4A16_SPLITK settings.  Returns "" and records the reason in
  * w4a16_last_error() for sizes the entry point would reject or for M = 0.
  * The string lives in static per-thread storage until the next call.
  */
 const char *w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul);
+/* The same query for nvfp4_gemv_splitk / bf16_gemv_splitk. */
+const char *w4a16_gemv_splitk_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul);
 
 /* Human-readable name of a status code (static storage).  The two names are
  * the same function. */

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["nvfp4_gemv", "bf16_gemv", "dequantize_rows", "moe_gate_up", "moe_down_combine",
                  "nvfp4_unswizzle_scales", "nvfp4_dequant_gemm", "nvfp4_dequant_gemm_workspace_bytes",
-                 "nvfp4_status_string", "w4a16_status_string", "w4a16_last_error"]:
+                 "nvfp4_status_string", "w4a16_status_string", "w4a16_last_error",
+                 "nvfp4_gemv_splitk", "bf16_gemv_splitk", "gemv_splitk_workspace_bytes"]:
         assert want in names
 
 
@@ -209,8 +210,81 @@ def test_gemv_kernel_name_query(monkeypatch):
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "valu")
     assert gemv_kernel_name(4, 4096, 4096).startswith("k_gemv_vchunk<4, false,")
-    assert gemv_kernel_name(64, 6144, 4096).endswith(", 2>")  # two row tiles per workgroup
-    assert gemv_kernel_name(64, 2 * 6144, 4096, silu_mul=True).endswith(", 1>")  # LDS: one with silu_mul
+    assert gemv_kernel_name(64, 6144, 4096).endswith(", 2, 1>")  # two row tiles per workgroup
+    assert gemv_kernel_name(64, 2 * 6144, 4096, silu_mul=True).endswith(", 1, 1>")  # LDS: one with silu_mul
     for bad in (dict(m=0, n=16, k=64), dict(m=65, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
         with pytest.raises(W4A16Error):
             gemv_kernel_name(bad["m"], bad["n"], bad["k"])
+
+
+def splitk(**kw):
+    lib = _lib.load()
+    a = dict(x=FAKE, M=32, K=8192, ldx=8192, w=FAKE, s=FAKE, gs=FAKE, N=1024, silu=0, ws=FAKE, wsb=None, out=FAKE)
+    a.update(kw)
+    wsb = a["wsb"] if a["wsb"] is not None else lib.gemv_splitk_workspace_bytes(1, a["M"], a["N"], a["K"], a["silu"])
+    return lib.nvfp4_gemv_splitk(a["x"], a["M"], a["K"], a["ldx"], a["w"], a["s"], a["gs"], a["N"], a["silu"],
+                                 a["ws"], wsb, a["out"], None)
+
+
+def test_splitk_plan_and_workspace_size(monkeypatch):
+    """The split plan (256 compute units assumed without a GPU): no split at
+    the sweep's shapes; one row tile per unit and 2 or 4 splits where the row
+    tiles would fill less than half the compute units; units of two tiles
+    over 2 splits where a workgroup would stream >= 768 KB of activations.
+    The workspace holds the counters (a 256-byte multiple) and the FP32
+    partials of every unit and split."""
+    from w4a16_nvfp4_gemv_amd import gemv_kernel_name
+    monkeypatch.delenv("W4A16_SPLITK", raising=False)
+    monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
+    lib = _lib.load()
+    for m in (1, 2, 4, 8, 16, 32, 64):
+        for n in (4096, 6144):
+            assert lib.gemv_splitk_workspace_bytes(1, m, n, 4096, 0) == 0
+            assert gemv_kernel_name(m, n, 4096, splitk=True) == gemv_kernel_name(m, n, 4096)
+    # 64 tiles, 4 splits: counters 256 bytes, 64 units x 4 splits x 1 A operand x NT x 1 KB
+    for m, xt in ((4, 4), (16, 16), (32, 32)):
+        nt = max(1, xt // 16)
+        assert gemv_kernel_name(m, 1024, 8192, splitk=True) == f"k_gemv_mfma<true, {xt}, false, 1, 4>"
+        assert lib.gemv_splitk_workspace_bytes(1, m, 1024, 8192, 0) == 256 + 64 * 4 * nt * 1024
+    assert gemv_kernel_name(4, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 4, false, 1, 1>"  # too little work
+    assert gemv_kernel_name(32, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 32, false, 1, 2>"
+    assert gemv_kernel_name(32, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 32, false, 2, 2>"
+    assert lib.gemv_splitk_workspace_bytes(1, 32, 4096, 14336, 0) == 512 + 128 * 2 * 2 * 2 * 1024
+    assert gemv_kernel_name(16, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 16, false, 1, 1>"
+    assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False, splitk=True) == "k_gemv_mfma<false, 32, false, 2, 2>"
+    assert gemv_kernel_name(32, 4096, 4096, silu_mul=True, splitk=True) == "k_gemv_mfma<true, 32, true, 1, 2>"
+    assert lib.gemv_splitk_workspace_bytes(1, 65, 4096, 4096, 0) == -1
+    assert lib.gemv_splitk_workspace_bytes(2, 32, 4096, 4096, 0) == -1
+    monkeypatch.setenv("W4A16_SPLITK", "off")
+    assert lib.gemv_splitk_workspace_bytes(1, 32, 1024, 8192, 0) == 0
+    assert gemv_kernel_name(32, 1024, 8192, splitk=True) == gemv_kernel_name(32, 1024, 8192)
+    monkeypatch.setenv("W4A16_SPLITK", "4,4")
+    assert gemv_kernel_name(32, 4096, 4096, splitk=True) == "k_gemv_mfma<true, 32, false, 4, 4>"
+    monkeypatch.setenv("W4A16_SPLITK", "5,3")  # not a built form: no split
+    assert lib.gemv_splitk_workspace_bytes(1, 32, 4096, 4096, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), INVALID),                 # the plan splits: a workspace is needed
+    (dict(wsb=4096), INVALID),                # too small
+    (dict(ws=FAKE + 64), MISALIGNED),         # 256-byte alignment
+    (dict(M=65), UNSUPPORTED),
+    (dict(s=FAKE + 2), MISALIGNED),
+    (dict(M=0, x=None, w=None, s=None, gs=None, ws=None, out=None), OK),
+])
+def test_nvfp4_gemv_splitk_argument_errors(kw, status, monkeypatch):
+    monkeypatch.delenv("W4A16_SPLITK", raising=False)
+    assert splitk(**kw) == status
+    if status != OK:
+        assert _lib.load().w4a16_last_error()
+
+
+def test_bf16_gemv_splitk_argument_errors(monkeypatch):
+    monkeypatch.delenv("W4A16_SPLITK", raising=False)
+    lib = _lib.load()
+    need = lib.gemv_splitk_workspace_bytes(0, 32, 4096, 14336, 0)
+    assert need > 0
+    assert lib.bf16_gemv_splitk(FAKE, 32, 14336, 14336, FAKE, 4096, 0, None, need, FAKE, None) == INVALID
+    assert lib.bf16_gemv_splitk(FAKE, 32, 14336, 14336, FAKE, 4096, 0, FAKE, need - 1, FAKE, None) == INVALID
+    assert lib.bf16_gemv_splitk(FAKE, 32, 14344, 14344, FAKE, 4096, 0, FAKE, need, FAKE, None) == UNSUPPORTED
+    assert lib.bf16_gemv_splitk(FAKE, 0, 4096, 4096, None, 4096, 0, None, 0, None, None) == OK

@@ -616,3 +616,149 @@ def test_moe_decode_block_full_size(m, moe_block_weights):
                              synth.MOE_HIDDEN)
     tokens = list(range(m)) if m <= 2 else [0, m // 2, m - 1]
     moe_check(wts, tok, act, sact, out, tokens, f"moe full M={m}")
+
+
+# ------------------------------------------------------------------ split-K (workspace entry points)
+SPLIT_FORMS = ["1,2", "2,2", "3,2", "4,2", "1,4", "2,4", "4,4"]
+
+
+def run_splitk(d, n, silu=False, ws=None, fp4=True):
+    if fp4:
+        out = lib.nvfp4_gemv_splitk(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]), silu_mul=silu, workspace=ws)
+    else:
+        out = lib.bf16_gemv_splitk(dev(d["x"]), dev(d["w"]), silu_mul=silu, workspace=ws)
+    torch.cuda.synchronize()
+    return to_bits(out.cpu())
+
+
+@pytest.mark.parametrize("form", SPLIT_FORMS)
+@pytest.mark.parametrize("m", [1, 4, 9, 16, 17, 32, 40, 64])
+@pytest.mark.parametrize("n,k,silu", [(256, 512, False), (400, 320, False), (4224, 128, False), (144, 4096, False),
+                                      (512, 1024, True), (288, 192, True)])
+def test_nvfp4_gemv_splitk_forms(form, m, n, k, silu, monkeypatch):
+    """Every built split-K form (row tiles per unit, splits) forced at token
+    counts of every staged tile size: ragged 128-row bands, more tiles than
+    compute units, splits with no K steps (K = 128 and 192 over 2 or 4
+    splits), silu_mul.  The counters are zero again after the call."""
+    monkeypatch.setenv("W4A16_SPLITK", form)
+    rt, s = map(int, form.split(","))
+    name = lib.gemv_kernel_name(m, n, k, silu_mul=silu, splitk=True)
+    split = name.endswith(f", {rt}, {s}>") and s > 1
+    _say("splitk", form, m, n, k, silu, name)
+    if name.startswith("k_gemv_mfma<") and lib._lib.load().gemv_splitk_workspace_bytes(1, m, n, k, int(silu)) > 0:
+        assert split, name  # the MFMA path takes the forced form whenever it fits
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 17 * n + k + rt)
+    ws = lib.gemv_splitk_workspace(m, n, k, silu, device=DEV)
+    got = run_splitk(d, n, silu, ws)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, d["gs"][0], f"splitk {form} silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, d["gs"][0], k, f"splitk {form} M={m} N={n} K={k}")
+    if not split:
+        assert int(ws.count_nonzero()) == 0, "workspace written without a split"
+    else:
+        tiles = ((n // 2 if silu else n) + 127) // 128 * 8
+        units = (tiles + rt - 1) // rt
+        assert int(ws[: units * 4].count_nonzero()) == 0, "arrival counters left non-zero"
+
+
+@pytest.mark.parametrize("form", ["2,2", "3,2", "4,4"])
+@pytest.mark.parametrize("m", [16, 32, 64])
+@pytest.mark.parametrize("n,k,silu", [(4096, 1024, False), (256, 4096, True), (96, 1040, False)])
+def test_bf16_gemv_splitk_forms(form, m, n, k, silu, monkeypatch):
+    monkeypatch.setenv("W4A16_SPLITK", form)
+    _say("bf16 splitk", form, m, n, k, silu)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 19 * n + k)
+    got = run_splitk(d, n, silu, None, fp4=False)
+    want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=silu)
+    if silu:
+        check_silu(got, want, acc, absacc, 1.0, f"bf16 splitk {form} silu M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, 1.0, k, f"bf16 splitk {form} M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fp4,m,n,k,silu", [
+    (True, 16, 4096, 4096, False), (True, 32, 6144, 4096, False),   # the sweep: no split, same as nvfp4_gemv
+    (True, 32, 4096, 14336, False), (True, 16, 1024, 8192, False), (True, 32, 1024, 8192, False),
+    (True, 4, 1024, 8192, False), (True, 32, 2048, 4096, False), (True, 32, 4096, 4096, True),
+    (False, 32, 4096, 14336, False), (False, 4, 2048, 8192, False), (False, 16, 1024, 4096, False)])
+def test_gemv_splitk_default_plan_full_size(fp4, m, n, k, silu, monkeypatch):
+    """The default split plan: every output element against the oracle, the
+    same bits on repeated calls that reuse the workspace, and where the plan
+    does not split, the same bits as the entry point without a workspace."""
+    monkeypatch.delenv("W4A16_SPLITK", raising=False)
+    name = lib.gemv_kernel_name(m, n, k, silu_mul=silu, weight_fp4=fp4, splitk=True)
+    _say("splitk default", fp4, m, n, k, silu, name)
+    if fp4:
+        d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m) + n + 3 * k)
+    else:
+        d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + n + 3 * k)
+    ws = lib.gemv_splitk_workspace(m, n, k, silu, weight_fp4=fp4, device=DEV)
+    got = run_splitk(d, n, silu, ws, fp4=fp4)
+    if fp4:
+        want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+        gs = d["gs"][0]
+    else:
+        want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=silu)
+        gs = 1.0
+    if silu:
+        check_silu(got, want, acc, absacc, gs, f"splitk {name} M={m} N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, gs, k, f"splitk {name} M={m} N={n} K={k}")
+    for _ in range(3):
+        assert np.array_equal(got, run_splitk(d, n, silu, ws, fp4=fp4)), "split-K result depends on the call"
+    split = name.startswith("k_gemv_mfma<") and name.rsplit(",", 1)[1].strip(" >") != "1"
+    if not split:
+        assert name == lib.gemv_kernel_name(m, n, k, silu_mul=silu, weight_fp4=fp4), name
+        plain = run_nvfp4(d, n, silu) if fp4 else run_bf16(d, silu)
+        assert np.array_equal(got, plain)
+
+
+def test_nvfp4_gemv_splitk_workspace_reuse_and_strided_x(monkeypatch):
+    """One workspace through calls of different sizes and forms (each leaves
+    its counters zero for the next), x with a row stride past K, and a
+    misaligned workspace rejected."""
+    monkeypatch.setenv("W4A16_SPLITK", "4,4")
+    big = lib.gemv_splitk_workspace(32, 4096, 1024, device=DEV)  # the largest call below
+    for m, n, k in ((32, 4096, 1024), (17, 256, 512), (64, 400, 320)):
+        d = synth.dense_w4a16(m, n, k, seed=700 + m)
+        wide = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+        wide[:, :k] = d["x"]
+        xv = dev(wide)[:, :k]
+        out = lib.nvfp4_gemv_splitk(xv, dev(d["w"]), dev(d["s"]), dev(d["gs"]), workspace=big)
+        torch.cuda.synchronize()
+        _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+        check_gemv(to_bits(out.cpu()), acc, absacc, d["gs"][0], k, f"splitk reuse M={m} N={n} K={k}")
+    d = synth.dense_w4a16(32, 256, 512, seed=777)
+    with pytest.raises(lib.W4A16Error):
+        lib.nvfp4_gemv_splitk(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]), workspace=big[16:])
+    with pytest.raises(lib.W4A16Error):
+        lib.nvfp4_gemv_splitk(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]), workspace=big[:256])
+
+
+@pytest.mark.parametrize("form", ["2,2", "4,4"])
+def test_nvfp4_gemv_splitk_alternating_inputs_share_a_workspace(form, monkeypatch):
+    """Two different input sets alternate on one workspace, 12 calls each:
+    every result equals that input's first (oracle-checked) result bit for
+    bit, so no call reads partial sums left by the previous one."""
+    monkeypatch.setenv("W4A16_SPLITK", form)
+    m, n, k = 32, 4096, 2048
+    ws = lib.gemv_splitk_workspace(m, n, k, device=DEV)
+    sets = [synth.dense_w4a16(m, n, k, seed=810 + i) for i in range(2)]
+    gpu = [{kk: dev(v) for kk, v in d.items()} for d in sets]
+    first = []
+    for d, g in zip(sets, gpu):
+        out = to_bits(lib.nvfp4_gemv_splitk(g["x"], g["w"], g["s"], g["gs"], workspace=ws).cpu())
+        _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+        check_gemv(out, acc, absacc, d["gs"][0], k, f"splitk alternating {form}")
+        first.append(out)
+    outs = []
+    for i in range(24):
+        g = gpu[i % 2]
+        outs.append(lib.nvfp4_gemv_splitk(g["x"], g["w"], g["s"], g["gs"], workspace=ws))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert np.array_equal(to_bits(o.cpu()), first[i % 2]), f"call {i} differs from its input's first result"
+    units = (n // 128 * 8) // int(form.split(",")[0])
+    assert int(ws[: units * 4].count_nonzero()) == 0, "arrival counters left non-zero"

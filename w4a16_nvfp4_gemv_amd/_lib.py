@@ -18,6 +18,9 @@ _int = ctypes.c_int
 SIGNATURES = {
     "nvfp4_gemv": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _p]),
     "bf16_gemv": (_int, [_p, _i64, _i64, _i64, _p, _i64, _int, _p, _p]),
+    "gemv_splitk_workspace_bytes": (_i64, [_int, _i64, _i64, _i64, _int]),
+    "nvfp4_gemv_splitk": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _i64, _p, _p]),
+    "bf16_gemv_splitk": (_int, [_p, _i64, _i64, _i64, _p, _i64, _int, _p, _i64, _p, _p]),
     "dequantize_rows": (_int, [_p, _p, _i64, _i64, _p, _p]),
     "nvfp4_dequant_gemm_workspace_bytes": (_i64, [_i64, _i64, _i64]),
     "nvfp4_dequant_gemm": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _i64, _p, _p]),
@@ -25,6 +28,7 @@ SIGNATURES = {
     "moe_gate_up": (_int, [_p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "moe_down_combine": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "w4a16_gemv_kernel_name": (ctypes.c_char_p, [_int, _i64, _i64, _i64, _int]),
+    "w4a16_gemv_splitk_kernel_name": (ctypes.c_char_p, [_int, _i64, _i64, _i64, _int]),
     "nvfp4_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_last_error": (ctypes.c_char_p, []),

@@ -57,40 +57,28 @@ int check_dense(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const void
   return W4A16_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* w4a16_status_string(int status) {
-  switch (status) {
-    case W4A16_OK: return "ok";
-    case W4A16_ERR_INVALID_ARG: return "invalid argument";
-    case W4A16_ERR_MISALIGNED: return "misaligned pointer or stride";
-    case W4A16_ERR_UNSUPPORTED: return "unsupported shape";
-    case W4A16_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-const char* nvfp4_status_string(int status) { return w4a16_status_string(status); }
-
-const char* w4a16_last_error(void) { return g_last_error.c_str(); }
-
-int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
-               const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
-               uint16_t* out, void* stream) {
-  int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 64);
+// The dense GEMV entry points.  With `splitk`, the call may use the
+// caller's workspace for the cross-workgroup split-K form (the plan for these
+// sizes says whether and how much).
+int run_gemv(bool fp4, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const void* w, const uint8_t* w_scale,
+             const float* global_scale, int64_t N, int silu_mul, void* workspace, int64_t workspace_bytes,
+             bool splitk, uint16_t* out, void* stream) {
+  int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, fp4 ? 64 : 16);
   if (st != W4A16_OK || M == 0) return st;
-  if (!w_scale || !global_scale) return fail(W4A16_ERR_INVALID_ARG, "null scale pointer");
-  if (!aligned(w_scale, 4) || !aligned(global_scale, 4)) return fail(W4A16_ERR_MISALIGNED, "w_scale and global_scale must be 4-byte aligned");
-  const int64_t w_bytes = N * (K / 2), s_bytes = flat_scale_bytes(N, K), x_bytes = ((M - 1) * ldx + K) * 2;
+  if (fp4) {
+    if (!w_scale || !global_scale) return fail(W4A16_ERR_INVALID_ARG, "null scale pointer");
+    if (!aligned(w_scale, 4) || !aligned(global_scale, 4))
+      return fail(W4A16_ERR_MISALIGNED, "w_scale and global_scale must be 4-byte aligned");
+  }
+  const int64_t w_bytes = fp4 ? N * (K / 2) : N * K * 2, s_bytes = fp4 ? flat_scale_bytes(N, K) : 0;
+  const int64_t x_bytes = ((M - 1) * ldx + K) * 2;
   if (w_bytes > kMaxDim || s_bytes > kMaxDim || x_bytes > kMaxDim)
     return fail(W4A16_ERR_UNSUPPORTED, "tensors above 2 GiB are not supported (weight %lld bytes)", w_bytes);
   w4a16::GemvParams p{};
   p.x = x;
-  p.w = w;
-  p.s = w_scale;
-  p.gs = global_scale;
+  p.w = static_cast<const uint8_t*>(w);
+  p.s = fp4 ? w_scale : nullptr;
+  p.gs = fp4 ? global_scale : nullptr;
   p.x_bytes = static_cast<uint32_t>(x_bytes);
   p.w_bytes = static_cast<uint32_t>(w_bytes);
   p.s_bytes = static_cast<uint32_t>(s_bytes);
@@ -100,39 +88,27 @@ int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8
   p.N = static_cast<int>(N);
   p.K = static_cast<int>(K);
   p.half = silu_mul ? static_cast<int>(N / 2) : 0;
+  if (splitk) {
+    const w4a16::SplitPlan plan = w4a16::gemv_split_plan(fp4, M, N, K, silu_mul);
+    if (plan.s > 1) {
+      if (!workspace) return fail(W4A16_ERR_INVALID_ARG, "null workspace (%lld bytes needed)", plan.bytes);
+      if (workspace_bytes < plan.bytes)
+        return fail(W4A16_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", workspace_bytes, plan.bytes);
+      if (!aligned(workspace, 256)) return fail(W4A16_ERR_MISALIGNED, "the workspace must be 256-byte aligned");
+      if (plan.bytes > kMaxDim) return fail(W4A16_ERR_UNSUPPORTED, "split-K workspace above 2 GiB (%lld bytes)", plan.bytes);
+      p.cnt = static_cast<uint32_t*>(workspace);
+      p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.cnt_bytes);
+      p.part_bytes = static_cast<uint32_t>(plan.bytes - plan.cnt_bytes);
+    }
+  }
   // The VALU kernels read a quad's scale words as one 16-byte chunk; a scale
   // buffer that is only 4-byte aligned goes to the MFMA kernels, which read
   // one 4-byte word per row.
-  const int path = aligned(w_scale, 16) ? w4a16::choose_gemv_path(true, M, N, K) : w4a16::kPathMfma;
-  return hip_status(w4a16::launch_gemv(true, p, silu_mul, path, static_cast<hipStream_t>(stream)));
+  const int path = (!fp4 || aligned(w_scale, 16)) ? w4a16::choose_gemv_path(fp4, M, N, K) : w4a16::kPathMfma;
+  return hip_status(w4a16::launch_gemv(fp4, p, silu_mul, path, static_cast<hipStream_t>(stream)));
 }
 
-int bf16_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w, int64_t N,
-              int silu_mul, uint16_t* out, void* stream) {
-  int st = check_dense(x, M, K, ldx, w, N, silu_mul, out, 16);
-  if (st != W4A16_OK || M == 0) return st;
-  const int64_t w_bytes = N * K * 2, x_bytes = ((M - 1) * ldx + K) * 2;
-  if (w_bytes > kMaxDim || x_bytes > kMaxDim)
-    return fail(W4A16_ERR_UNSUPPORTED, "tensors above 2 GiB are not supported (weight %lld bytes)", w_bytes);
-  w4a16::GemvParams p{};
-  p.x = x;
-  p.w = reinterpret_cast<const uint8_t*>(w);
-  p.s = nullptr;
-  p.gs = nullptr;
-  p.x_bytes = static_cast<uint32_t>(x_bytes);
-  p.w_bytes = static_cast<uint32_t>(w_bytes);
-  p.s_bytes = 0;
-  p.out = out;
-  p.ldx = ldx;
-  p.M = static_cast<int>(M);
-  p.N = static_cast<int>(N);
-  p.K = static_cast<int>(K);
-  p.half = silu_mul ? static_cast<int>(N / 2) : 0;
-  const int path = w4a16::choose_gemv_path(false, M, N, K);
-  return hip_status(w4a16::launch_gemv(false, p, silu_mul, path, static_cast<hipStream_t>(stream)));
-}
-
-const char* w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul) {
+const char* gemv_kernel_name_of(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul, bool splitk) {
   thread_local char name[128];
   name[0] = 0;
   if (weight_fp4 != 0 && weight_fp4 != 1) {
@@ -155,10 +131,78 @@ const char* w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t
   p.K = static_cast<int>(K);
   p.half = silu_mul ? static_cast<int>(N / 2) : 0;
   const bool fp4 = weight_fp4 != 0;
+  if (splitk && w4a16::gemv_split_plan(fp4, M, N, K, silu_mul).s > 1) {
+    // a stand-in workspace: the dispatch only checks that there is one
+    p.part = reinterpret_cast<float*>(uintptr_t(256));
+    p.cnt = reinterpret_cast<uint32_t*>(uintptr_t(256));
+  }
   w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, M, N, K), name, sizeof name);
   ok();
   return name;
 }
+
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported shape";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_status_string(int status) { return w4a16_status_string(status); }
+
+const char* w4a16_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
+               const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
+               uint16_t* out, void* stream) {
+  return run_gemv(true, x, M, K, ldx, w, w_scale, global_scale, N, silu_mul, nullptr, 0, false, out, stream);
+}
+
+int bf16_gemv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w, int64_t N,
+              int silu_mul, uint16_t* out, void* stream) {
+  return run_gemv(false, x, M, K, ldx, w, nullptr, nullptr, N, silu_mul, nullptr, 0, false, out, stream);
+}
+
+int64_t gemv_splitk_workspace_bytes(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul) {
+  if (weight_fp4 != 0 && weight_fp4 != 1) return -1;
+  const uint16_t* stand_in = reinterpret_cast<const uint16_t*>(uintptr_t(256));
+  if (check_dense(stand_in, M, K, K, stand_in, N, silu_mul, reinterpret_cast<uint16_t*>(uintptr_t(256)),
+                  weight_fp4 ? 64 : 16) != W4A16_OK)
+    return -1;
+  ok();
+  return M == 0 ? 0 : w4a16::gemv_split_plan(weight_fp4 != 0, M, N, K, silu_mul).bytes;
+}
+
+int nvfp4_gemv_splitk(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
+                      const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
+                      void* workspace, int64_t workspace_bytes, uint16_t* out, void* stream) {
+  return run_gemv(true, x, M, K, ldx, w, w_scale, global_scale, N, silu_mul, workspace, workspace_bytes, true, out,
+                  stream);
+}
+
+int bf16_gemv_splitk(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w, int64_t N,
+                     int silu_mul, void* workspace, int64_t workspace_bytes, uint16_t* out, void* stream) {
+  return run_gemv(false, x, M, K, ldx, w, nullptr, nullptr, N, silu_mul, workspace, workspace_bytes, true, out,
+                  stream);
+}
+
+const char* w4a16_gemv_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul) {
+  return gemv_kernel_name_of(weight_fp4, M, N, K, silu_mul, false);
+}
+
+const char* w4a16_gemv_splitk_kernel_name(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul) {
+  return gemv_kernel_name_of(weight_fp4, M, N, K, silu_mul, true);
+}
+
 
 int dequantize_rows(const uint8_t* w, const uint8_t* w_scale, int64_t rows, int64_t K,
                     uint16_t* out, void* stream) {

@@ -475,20 +475,64 @@ constexpr int mfma_waves(int /*XT*/) { return 4; }
 // (deeper rings were slower).  Bounded by vmcnt, which counts at most 63 outstanding loads, and by
 // the LDS ring (128 KB per workgroup).  A depth that divides the steps of a
 // wave wastes nothing in the last round; K = 4096 gives 8 steps per wave.
-template <bool FP4, int XT, int NA, int W>
-constexpr int mfma_depth() {
-  const int per = FP4 ? 2 : 4;                   // loads per A operand and step
+constexpr int mfma_depth_of(bool fp4, int xt, int na, int w) {
+  const int per = fp4 ? 2 : 4;                   // loads per A operand and step
   const int cpt = 16;                            // 16-byte chunks per token and step
-  const int load_x = XT * cpt / 64;              // staging loads per step
-  int d = (XT >= 32 || (!FP4 && XT >= 16)) ? 2 : 4;
-  while (d > 2 && (NA * per + (d - 1) * (load_x + NA * per) > 62 || W * d * XT * cpt * 16 > 128 * 1024)) d /= 2;
+  const int load_x = xt * cpt / 64;              // staging loads per step
+  int d = (xt >= 32 || (!fp4 && xt >= 16)) ? 2 : 4;
+  while (d > 2 && (na * per + (d - 1) * (load_x + na * per) > 62 || w * d * xt * cpt * 16 > 128 * 1024)) d /= 2;
   return d;
+}
+
+template <bool FP4, int XT, int NA, int W>
+constexpr int mfma_depth() { return mfma_depth_of(FP4, XT, NA, W); }
+
+// Whether the MFMA kernel with na A operands per step fits a compute unit:
+// the loads a full ring keeps in flight within vmcnt's count, and the ring
+// plus the cross-wave partial sums within the 160 KB of LDS.
+constexpr bool mfma_fits(bool fp4, int xt, int na) {
+  const int w = mfma_waves(xt);
+  const int d = mfma_depth_of(fp4, xt, na, w);
+  const int per = fp4 ? 2 : 4;
+  const int l = xt * 16 / 64 + na * per;
+  const int nt = (xt + 15) / 16;
+  return na * per + (d - 1) * l <= 62 && d * w * xt * 256 + (w - 1) * na * nt * 64 * 16 <= 160 * 1024;
 }
 
 // XT: token rows staged per step (4, 8, 16, 32 or 64).  With XT < 16 the fragment
 // lanes of tokens XT..15 read the rows of tokens 0..XT-1 again: those MFMA
 // columns are never stored.
-template <bool FP4, int XT, bool SILU, int RT>
+//
+// S > 1: cross-workgroup split-K.  Every workgroup streams all M*K*2 bytes
+// of activations for its K range, so from 16 tokens on the activation bytes
+// that reach the compute units exceed the weight bytes several times.  With
+// S splits, S workgroups share a unit of RT row tiles, each taking 1/S of
+// K, so the activation stream per workgroup shrinks S-fold for the same
+// weight bytes.  Items are numbered split-major: the workgroups of one XCD
+// share a K range (and its activations in their L2).  Each workgroup
+// writes its FP32 partial sums to the workspace, and the last of the S to
+// arrive at the unit's counter adds the S partials in split order (the same
+// sum whatever the arrival order), applies the epilogue and clears the
+// counter for the next call.
+//
+// Hand-off.  The partial sums are written and read with device-coherent
+// (sc1) buffer accesses, which is how the compiler implements relaxed
+// device-scope atomic loads and stores: they do not stop in an XCD's L2.
+// A writer waits for its stores (vmcnt 0) before its counter increment, and
+// the last arriver issues its loads only after the increment has returned,
+// so it reads every other split's sums.  A __threadfence() here would write
+// back and invalidate the whole L2 of the XCD on every arrival, which
+// measured 2-4x slower than the call without a split.
+constexpr int kCoherent = 16;  // cache policy bit sc1 of the buffer intrinsics
+
+__device__ __forceinline__ void store16_coherent(rsrc_t r, uint32_t off, const f32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, static_cast<int>(off), 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 load16_coherent(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCoherent));
+}
+
+template <bool FP4, int XT, bool SILU, int RT, int S>
 __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvParams p) {
   constexpr int NT = (XT + 15) / 16;        // token tiles (B operands)
   constexpr int NA = (SILU ? 2 : 1) * RT;   // A operands per step: RT row tiles (x gate, up)
@@ -514,7 +558,8 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
   const int64_t limit = SILU ? p.half : p.N;
   const uint32_t row_bytes = FP4 ? p.K / 2 : static_cast<uint32_t>(p.K) * 2;
   const int64_t steps_total = (p.K + KSTEP - 1) / KSTEP;
-  const int64_t spw = (steps_total + W - 1) / W;       // steps per wave
+  const int64_t sps = S == 1 ? steps_total : (steps_total + S - 1) / S;  // steps per split
+  const int64_t spw = (sps + W - 1) / W;               // steps per wave
   static_assert((W & (W - 1)) == 0, "the slice rotation below needs a power-of-two wave count");
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
   const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
@@ -531,14 +576,19 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
     sxo[i] = t < p.M ? static_cast<uint32_t>(t) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
   }
 
-  for (int64_t tile = xcd_logical_block(); tile < p.units; tile += gridDim.x) {
+  for (int64_t item = xcd_logical_block(); item < p.units * S; item += gridDim.x) {
+    const int64_t split = S == 1 ? 0 : item / p.units;
+    const int64_t tile = S == 1 ? item : item - split * p.units;  // the unit of RT row tiles
+    const int64_t s_first = split * sps;                          // this split's steps
+    const int64_t s_count = s_first < steps_total ? (steps_total - s_first < sps ? steps_total - s_first : sps) : 0;
     // This wave's K slice.  From 8 staged tokens on, the slices rotate with
     // the tile, so that the workgroups of one die do not all stream the same
     // activation slice at the same time (measured 2-6% faster at 8..32 tokens,
     // and slower at 4).
     const int slice = XT >= 8 ? (wave + static_cast<int>(tile & (W - 1))) & (W - 1) : wave;
-    const int64_t st0 = slice * spw;
-    const int64_t nst = st0 < steps_total ? (steps_total - st0 < spw ? steps_total - st0 : spw) : 0;
+    const int64_t w0 = slice * spw;
+    const int64_t st0 = s_first + w0;
+    const int64_t nst = w0 < s_count ? (s_count - w0 < spw ? s_count - w0 : spw) : 0;
     // A operand a: row tile tile*RT + a % RT, the up half for a >= RT
     int64_t rows[NA];
     bool rv[NA];
@@ -656,22 +706,55 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
         for (int a = 0; a < NA; ++a)
 #pragma unroll
           for (int n = 0; n < NT; ++n) acc[a][n] += red[w][a][n][lane];
-      // C layout: lane holds rows 4(l/16)+i of the tile, token column l%16
+      bool last = true;
+      if constexpr (S > 1) {
+        // publish this split's partial sums, then count the arrival.  The
+        // partials of (unit, split) are NA * NT * 64 f32x4, lane-minor.
+        const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+        auto part_off = [&](int64_t s2, int a, int n) {
+          return static_cast<uint32_t>((((tile * S + s2) * NA + a) * NT + n) * 64 + lane) * 16u;
+        };
 #pragma unroll
-      for (int a = 0; a < RT; ++a) {
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int m = 16 * n + (lane & 15);
+          for (int n = 0; n < NT; ++n) store16_coherent(rp, part_off(split, a, n), acc[a][n]);
+        vm_wait<0>();  // the partial sums are visible device-wide before the count
+        uint32_t before = 0;
+        if (lane == 0) before = atomicAdd(p.cnt + tile, 1u);
+        last = __builtin_amdgcn_readfirstlane(before) == S - 1;
+        asm volatile("" ::: "memory");  // the loads below stay after the count
+        if (last) {
+          // the S partials in split order (this workgroup's own from registers)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t row = mfma_row<FP4>(tile * RT + a, 4 * (lane >> 4) + i);
-            if (m >= p.M || row >= limit) continue;
-            if constexpr (!SILU) {
-              p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(acc[a][n][i] * gs);
-            } else {
-              const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[a][n][i] * gs));
-              const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[RT + a][n][i] * gs));
-              p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+          for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              f32x4 t = split == 0 ? acc[a][n] : load16_coherent(rp, part_off(0, a, n));
+#pragma unroll
+              for (int s2 = 1; s2 < S; ++s2) t += s2 == split ? acc[a][n] : load16_coherent(rp, part_off(s2, a, n));
+              acc[a][n] = t;
+            }
+          if (lane == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (last) {
+        // C layout: lane holds rows 4(l/16)+i of the tile, token column l%16
+#pragma unroll
+        for (int a = 0; a < RT; ++a) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const int m = 16 * n + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int64_t row = mfma_row<FP4>(tile * RT + a, 4 * (lane >> 4) + i);
+              if (m >= p.M || row >= limit) continue;
+              if constexpr (!SILU) {
+                p.out[m * static_cast<int64_t>(p.N) + row] = f32_to_bf16_bits(acc[a][n][i] * gs);
+              } else {
+                const float gv = bf16_bits_to_f32(f32_to_bf16_bits(acc[a][n][i] * gs));
+                const float uv = bf16_bits_to_f32(f32_to_bf16_bits(acc[RT + a][n][i] * gs));
+                p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(gv) * uv);
+              }
             }
           }
         }
@@ -972,18 +1055,18 @@ hipError_t launch_valu(const GemvParams& p, int lpq, hipStream_t stream) {
   }
 }
 
-template <bool FP4, int XT, bool SILU, int RT>
+template <bool FP4, int XT, bool SILU, int RT, int S = 1>
 hipError_t launch_mfma_rt(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
   p.units = (tiles + RT - 1) / RT;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s, %d>", tf(FP4), XT, tf(SILU), RT);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_mfma<%s, %d, %s, %d, %d>", tf(FP4), XT, tf(SILU), RT, S);
     return hipSuccess;
   }
-  int64_t blocks = p.units;
+  int64_t blocks = p.units * S;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((k_gemv_mfma<FP4, XT, SILU, RT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((k_gemv_mfma<FP4, XT, SILU, RT, S>), dim3(static_cast<unsigned>(blocks)),
                      dim3(mfma_waves(XT) * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -1031,10 +1114,38 @@ bool launch_mfma_bd(GemvParams p, hipStream_t stream, hipError_t* err) {
 // round instead of leaving some units with twice the work of the others.
 int mfma_row_tiles(int64_t tiles) { return tiles > device_cu_count() ? 2 : 1; }
 
+// Token rows the MFMA kernels stage per step for M tokens.
+int mfma_xt(int64_t M) { return M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+
+// The split-K forms built into the library: (row tiles per unit, splits).
+constexpr int kSplitForms[][2] = {{1, 2}, {2, 2}, {3, 2}, {4, 2}, {1, 4}, {2, 4}, {4, 4}};
+
+template <bool FP4, int XT, bool SILU, int RT, int S>
+bool launch_split_if(const GemvParams& p, int rt, int s, hipStream_t stream, hipError_t* err) {
+  if (rt != RT || s != S) return false;
+  if constexpr (mfma_fits(FP4, XT, (SILU ? 2 : 1) * RT)) {
+    *err = launch_mfma_rt<FP4, XT, SILU, RT, S>(p, stream);
+    return true;
+  }
+  return false;
+}
+
 template <bool FP4, int XT, bool SILU>
 hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
   const int64_t tiles = FP4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  if (p.part != nullptr) {
+    const SplitPlan plan = gemv_split_plan(FP4, p.M, p.N, p.K, SILU);
+    hipError_t err = hipSuccess;
+    if (plan.s > 1 && (launch_split_if<FP4, XT, SILU, 1, 2>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 2, 2>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 3, 2>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 4, 2>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 1, 4>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 2, 4>(p, plan.rt, plan.s, stream, &err) ||
+                       launch_split_if<FP4, XT, SILU, 4, 4>(p, plan.rt, plan.s, stream, &err)))
+      return err;
+  }
   // (one tile per workgroup at XT = 4, and for silu_mul up to XT = 8:
   // measured faster there; with silu_mul at XT = 64 a second tile's partial
   // sums would not fit in LDS beside the ring)
@@ -1077,6 +1188,59 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
 
 }  // namespace
 
+SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
+  SplitPlan none{1, 1, 0};
+  if (M <= 0 || N <= 0 || K <= 0) return none;
+  const int xt = mfma_xt(M);
+  const int64_t limit = silu ? N / 2 : N;
+  const int64_t tiles = fp4 ? ((limit + 127) / 128) * 8 : (limit + 15) / 16;
+  int rt = 1, s = 1;
+  const char* env = std::getenv("W4A16_SPLITK");
+  if (env && std::strcmp(env, "off") == 0) return none;
+  if (env && std::sscanf(env, "%d,%d", &rt, &s) == 2) {
+    // a forced form (tests and measurements); it must be one of the built ones
+    bool built = false;
+    for (const auto& f : kSplitForms) built |= f[0] == rt && f[1] == s;
+    if (!built) return none;
+  } else {
+    // Measured on the MI355X (graphs of 64 launches, rotating weights): the
+    // hand-off of the partial sums costs about 1.2 us, so a split pays where
+    // it either fills compute units that would idle or removes a large share
+    // of the activation stream.
+    //  * Fewer row tiles than half the compute units: one tile per unit and
+    //    2 splits (4 where a quarter of the units would be busy and each
+    //    split still streams >= 16 KB of weights), once a workgroup's weight
+    //    and activation bytes reach 160 KB (128 KB with 4 splits).  E.g.
+    //    1024 x 8192 NVFP4 at 32 tokens 11.9 -> 7.8 us, BF16 2048 x 8192
+    //    13.5 -> 9.6 us at 4 tokens; 1024 x 4096 NVFP4 at 4 tokens stays.
+    //  * Otherwise, when a workgroup would stream >= 768 KB of activations:
+    //    2 splits over units of about 2 * tiles / (compute units) tiles.
+    //    E.g. 4096 x 14336 NVFP4 at 32 tokens 21.4 -> 17.4 us, BF16 36.5 ->
+    //    31.6 us; the 4096 x 4096 and 6144 x 4096 sweep shapes never split.
+    if (fp4 && M <= kValuMaxMFp4) return none;  // the VALU kernels take these
+    const int64_t cus = device_cu_count();
+    const double w_tile = 16.0 * (silu ? 2 : 1) * static_cast<double>(K) * (fp4 ? 0.5625 : 2.0);
+    const double a_wg = static_cast<double>(xt) * static_cast<double>(K) * 2.0;
+    if (tiles * 2 <= cus) {
+      rt = 1;
+      s = (tiles * 4 <= cus && w_tile / 4 >= 16384.0) ? 4 : 2;
+      if (w_tile + a_wg < (s == 4 ? 131072.0 : 163840.0)) return none;
+    } else if (a_wg >= 786432.0) {
+      s = 2;
+      const int64_t want = (tiles * s + cus - 1) / cus;
+      rt = static_cast<int>(want < 1 ? 1 : want > 4 ? 4 : want);
+    } else {
+      return none;
+    }
+  }
+  const int na = (silu ? 2 : 1) * rt;
+  if (!mfma_fits(fp4, xt, na)) return none;
+  const int64_t units = (tiles + rt - 1) / rt;
+  const int64_t nt = (xt + 15) / 16;
+  const int64_t cnt_bytes = (units * 4 + 255) / 256 * 256;
+  return SplitPlan{rt, s, cnt_bytes, cnt_bytes + units * s * na * nt * 64 * 16};
+}
+
 // VALU dot path for the smallest M and the MFMA path above it.  NVFP4 rows
 // of up to kVchunkMaxK columns take the chunked VALU kernel (M <= 4); other
 // VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
@@ -1100,7 +1264,7 @@ void describe_gemv(bool fp4, const GemvParams& p, int silu, int path, char* name
   name[0] = 0;
   t_describe = name;
   t_describe_len = len;
-  (void)launch_gemv(fp4, p, silu, path, nullptr);
+  (void)launch_gemv(fp4, p, silu, path, nullptr);  // p.part non-null: the form with a workspace
   t_describe = nullptr;
   t_describe_len = 0;
 }

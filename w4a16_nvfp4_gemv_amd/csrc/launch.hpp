@@ -24,7 +24,23 @@ struct GemvParams {
   uint32_t s_bytes;     // out-of-range loads return zero
   int M, N, K;
   int half;            // N / 2 with silu_mul, else 0
+  // Cross-workgroup split-K (MFMA kernels): FP32 partial sums and per-unit
+  // arrival counters (zero between calls) in a caller-provided workspace;
+  // null when the call has no workspace.
+  float* part;
+  uint32_t* cnt;
+  uint32_t part_bytes;  // extent of part (below 2 GiB)
 };
+
+// The split-K form a GEMV call uses when it has a workspace: rt row tiles
+// per unit and s workgroups per unit along K (s == 1: no split), and the
+// workspace bytes that form needs (0 for s == 1).
+struct SplitPlan {
+  int rt, s;
+  int64_t cnt_bytes;  // the counters, at the start of the workspace (256-byte multiple)
+  int64_t bytes;      // counters and partial sums
+};
+SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
 
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream);

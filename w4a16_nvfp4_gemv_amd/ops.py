@@ -88,6 +88,70 @@ def bf16_gemv(x: torch.Tensor, weight: torch.Tensor, silu_mul: bool = False,
     return out
 
 
+def gemv_splitk_workspace(m: int, n: int, k: int, silu_mul: bool = False, weight_fp4: bool = True,
+                          device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for nvfp4_gemv_splitk / bf16_gemv_splitk at
+    these sizes (at least 256 bytes, so that one buffer also serves calls
+    whose plan uses no split).  Every call leaves its counters zero, so the
+    buffer can be reused by calls that do not overlap."""
+    nbytes = _lib.load().gemv_splitk_workspace_bytes(int(weight_fp4), m, n, k, int(bool(silu_mul)))
+    if nbytes < 0:
+        raise W4A16Error(1, "gemv_splitk_workspace_bytes")
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _workspace(ws: torch.Tensor):
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("the workspace must be a contiguous uint8 tensor")
+    return ws.data_ptr(), ws.numel()
+
+
+def nvfp4_gemv_splitk(x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor,
+                      global_scale: torch.Tensor, silu_mul: bool = False,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_gemv with a workspace for the cross-workgroup K split (a fresh
+    zeroed one when none is given)."""
+    x = _x2d(x)
+    if weight.dtype != torch.uint8 or weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous uint8 [N, K/2] tensor")
+    m, k = x.shape[0], weight.shape[1] * 2
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weight needs K={k}")
+    n = weight.shape[0]
+    gs = global_scale.reshape(1)
+    if gs.dtype != torch.float32:
+        raise ValueError("global_scale must be float32")
+    scale = _flat_u8(weight_scale)
+    if workspace is None:
+        workspace = gemv_splitk_workspace(m, n, k, silu_mul, True, x.device)
+    wp, wn = _workspace(workspace)
+    out = torch.empty((m, n // 2 if silu_mul else n), dtype=torch.bfloat16, device=x.device)
+    st = _lib.load().nvfp4_gemv_splitk(x.data_ptr(), m, k, x.stride(0), weight.data_ptr(), scale.data_ptr(),
+                                       gs.data_ptr(), n, int(bool(silu_mul)), wp, wn, out.data_ptr(), _stream(x))
+    _check(st, "nvfp4_gemv_splitk")
+    return out
+
+
+def bf16_gemv_splitk(x: torch.Tensor, weight: torch.Tensor, silu_mul: bool = False,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16_gemv with a workspace for the cross-workgroup K split."""
+    x = _x2d(x)
+    if weight.dtype != torch.bfloat16 or weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous bfloat16 [N, K] tensor")
+    m, k = x.shape[0], weight.shape[1]
+    if x.shape[1] < k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weight needs K={k}")
+    n = weight.shape[0]
+    if workspace is None:
+        workspace = gemv_splitk_workspace(m, n, k, silu_mul, False, x.device)
+    wp, wn = _workspace(workspace)
+    out = torch.empty((m, n // 2 if silu_mul else n), dtype=torch.bfloat16, device=x.device)
+    st = _lib.load().bf16_gemv_splitk(x.data_ptr(), m, k, x.stride(0), weight.data_ptr(), n, int(bool(silu_mul)),
+                                      wp, wn, out.data_ptr(), _stream(x))
+    _check(st, "bf16_gemv_splitk")
+    return out
+
+
 def dequant_gemm(x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor,
                  global_scale: torch.Tensor, silu_mul: bool = False) -> torch.Tensor:
     """The nvfp4_gemv result for any number of tokens, by dequantize + library GEMM."""
@@ -136,11 +200,14 @@ def nvfp4_unswizzle_scales(weight_scale: torch.Tensor, n: int, k: int) -> torch.
     return out
 
 
-def gemv_kernel_name(m: int, n: int, k: int, silu_mul: bool = False, weight_fp4: bool = True) -> str:
-    """Name of the kernel nvfp4_gemv (or bf16_gemv) launches for these sizes
-    (host-only query; raises W4A16Error for sizes the entry point rejects)."""
+def gemv_kernel_name(m: int, n: int, k: int, silu_mul: bool = False, weight_fp4: bool = True,
+                     splitk: bool = False) -> str:
+    """Name of the kernel nvfp4_gemv (or bf16_gemv; with splitk the _splitk
+    entry points) launches for these sizes (host-only query; raises
+    W4A16Error for sizes the entry point rejects)."""
     lib = _lib.load()
-    name = lib.w4a16_gemv_kernel_name(int(weight_fp4), m, n, k, int(silu_mul)).decode()
+    query = lib.w4a16_gemv_splitk_kernel_name if splitk else lib.w4a16_gemv_kernel_name
+    name = query(int(weight_fp4), m, n, k, int(silu_mul)).decode()
     if not name:
         raise W4A16Error(1, "gemv_kernel_name")
     return name
