@@ -105,10 +105,12 @@ int bf16_gemv(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  *   Arguments as nvfp4_gemv / bf16_gemv, plus:
  *   workspace        device memory owned by the caller, 256-byte aligned, of
  *                    at least gemv_splitk_workspace_bytes(...) bytes for these
- *                    sizes.  Its first bytes are per-unit arrival counters:
- *                    they must be ZERO before the first call (e.g. memset
- *                    once after allocation); every call leaves them zero.
- *                    Calls that share a workspace must not overlap.
+ *                    sizes.  Its first 64 KiB hold per-unit arrival counters
+ *                    (for every shape): they must be ZERO before the first
+ *                    call (e.g. memset once after allocation), and every call
+ *                    leaves them zero, so one workspace of the largest size
+ *                    serves calls of any sizes.  Calls that share a workspace
+ *                    must not overlap.
  *   workspace_bytes  its size.
  * When the plan for these sizes uses no split (the size query returns 0),
  * workspace may be NULL and the call is exactly nvfp4_gemv / bf16_gemv.

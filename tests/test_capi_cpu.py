@@ -231,7 +231,7 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
     the sweep's shapes; one row tile per unit and 2 or 4 splits where the row
     tiles would fill less than half the compute units; units of two tiles
     over 2 splits where a workgroup would stream >= 768 KB of activations.
-    The workspace holds the counters (a 256-byte multiple) and the FP32
+    The workspace holds 64 KiB of counters (whatever the plan) and the FP32
     partials of every unit and split."""
     from w4a16_nvfp4_gemv_amd import gemv_kernel_name
     monkeypatch.delenv("W4A16_SPLITK", raising=False)
@@ -241,15 +241,15 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
         for n in (4096, 6144):
             assert lib.gemv_splitk_workspace_bytes(1, m, n, 4096, 0) == 0
             assert gemv_kernel_name(m, n, 4096, splitk=True) == gemv_kernel_name(m, n, 4096)
-    # 64 tiles, 4 splits: counters 256 bytes, 64 units x 4 splits x 1 A operand x NT x 1 KB
+    # 64 tiles, 4 splits: 64 KiB of counters, 64 units x 4 splits x 1 A operand x NT x 1 KB
     for m, xt in ((4, 4), (16, 16), (32, 32)):
         nt = max(1, xt // 16)
         assert gemv_kernel_name(m, 1024, 8192, splitk=True) == f"k_gemv_mfma<true, {xt}, false, 1, 4>"
-        assert lib.gemv_splitk_workspace_bytes(1, m, 1024, 8192, 0) == 256 + 64 * 4 * nt * 1024
+        assert lib.gemv_splitk_workspace_bytes(1, m, 1024, 8192, 0) == 65536 + 64 * 4 * nt * 1024
     assert gemv_kernel_name(4, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 4, false, 1, 1>"  # too little work
     assert gemv_kernel_name(32, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 32, false, 1, 2>"
     assert gemv_kernel_name(32, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 32, false, 2, 2>"
-    assert lib.gemv_splitk_workspace_bytes(1, 32, 4096, 14336, 0) == 512 + 128 * 2 * 2 * 2 * 1024
+    assert lib.gemv_splitk_workspace_bytes(1, 32, 4096, 14336, 0) == 65536 + 128 * 2 * 2 * 2 * 1024
     assert gemv_kernel_name(16, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 16, false, 1, 1>"
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False, splitk=True) == "k_gemv_mfma<false, 32, false, 2, 2>"
     assert gemv_kernel_name(32, 4096, 4096, silu_mul=True, splitk=True) == "k_gemv_mfma<true, 32, true, 1, 2>"

@@ -1236,9 +1236,13 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   const int na = (silu ? 2 : 1) * rt;
   if (!mfma_fits(fp4, xt, na)) return none;
   const int64_t units = (tiles + rt - 1) / rt;
+  if (units * 4 > kSplitCounterBytes) return none;
   const int64_t nt = (xt + 15) / 16;
-  const int64_t cnt_bytes = (units * 4 + 255) / 256 * 256;
-  return SplitPlan{rt, s, cnt_bytes, cnt_bytes + units * s * na * nt * 64 * 16};
+  // The counters sit in a region of fixed size at the start of every
+  // workspace, whatever the plan: partial sums of one call never overlap
+  // counters of another, so a workspace moves between shapes with every
+  // counter still zero.
+  return SplitPlan{rt, s, kSplitCounterBytes, kSplitCounterBytes + units * s * na * nt * 64 * 16};
 }
 
 // VALU dot path for the smallest M and the MFMA path above it.  NVFP4 rows

@@ -37,9 +37,12 @@ struct GemvParams {
 // workspace bytes that form needs (0 for s == 1).
 struct SplitPlan {
   int rt, s;
-  int64_t cnt_bytes;  // the counters, at the start of the workspace (256-byte multiple)
+  int64_t cnt_bytes;  // the counters, at the start of the workspace (kSplitCounterBytes)
   int64_t bytes;      // counters and partial sums
 };
+// Bytes of arrival counters at the start of every split-K workspace (one
+// 32-bit counter per unit: plans with more units do not split).
+constexpr int64_t kSplitCounterBytes = 65536;
 SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
 
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
