@@ -131,6 +131,26 @@ int bf16_gemv_splitk(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const
                      uint16_t *out, void *stream);
 
 /*
+ * nvfp4_gemv_splitk_noalloc -- nvfp4_gemv_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid it): the same kernels and the same
+ * results, with the split-K partial sums and counters in a scratch array
+ * that the library holds on each GPU (W4A16_NOALLOC_SCRATCH_BYTES, created
+ * with the library's code object on that device and kept until the process
+ * ends).  No call allocates or frees memory.  Arguments as nvfp4_gemv.
+ * All calls on one GPU share that GPU's scratch: calls that may overlap
+ * (different streams without ordering between them) race and must not be
+ * issued.  Every call leaves the scratch's counters zero for the next one.
+ * Returns W4A16_ERR_UNSUPPORTED when the split plan for these sizes needs
+ * more scratch than W4A16_NOALLOC_SCRATCH_BYTES (w4a16_last_error() gives
+ * both sizes), otherwise the errors of nvfp4_gemv.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (8ll << 20)
+int nvfp4_gemv_splitk_noalloc(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                              const uint8_t *w, const uint8_t *w_scale, const float *global_scale,
+                              int64_t N, int silu_mul, uint16_t *out, void *stream);
+
+/*
  * dequantize_rows -- out[rows][K] = bf16(e2m1 * e4m3), bit-exact, global
  * scale not applied (nvfp4_gemv page, function dequantize_rows).
  * Needs rows % 16 == 0 and K % 256 == 0 (the page's assertion).

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for want in ["nvfp4_gemv", "bf16_gemv", "dequantize_rows", "moe_gate_up", "moe_down_combine",
                  "nvfp4_unswizzle_scales", "nvfp4_dequant_gemm", "nvfp4_dequant_gemm_workspace_bytes",
                  "nvfp4_status_string", "w4a16_status_string", "w4a16_last_error",
-                 "nvfp4_gemv_splitk", "bf16_gemv_splitk", "gemv_splitk_workspace_bytes"]:
+                 "nvfp4_gemv_splitk", "bf16_gemv_splitk", "gemv_splitk_workspace_bytes",
+                 "nvfp4_gemv_splitk_noalloc"]:
         assert want in names
 
 
@@ -288,3 +289,17 @@ def test_bf16_gemv_splitk_argument_errors(monkeypatch):
     assert lib.bf16_gemv_splitk(FAKE, 32, 14336, 14336, FAKE, 4096, 0, FAKE, need - 1, FAKE, None) == INVALID
     assert lib.bf16_gemv_splitk(FAKE, 32, 14344, 14344, FAKE, 4096, 0, FAKE, need, FAKE, None) == UNSUPPORTED
     assert lib.bf16_gemv_splitk(FAKE, 0, 4096, 4096, None, 4096, 0, None, 0, None, None) == OK
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch(monkeypatch):
+    """The entry point that allocates nothing checks the split plan's scratch
+    against the library's fixed size before any HIP call."""
+    lib = _lib.load()
+    monkeypatch.setenv("W4A16_SPLITK", "1,4")
+    # 65536 rows at 64 tokens over 4 splits: 4096 units x 4 x 4 token tiles x 1 KB = 64 MiB
+    assert lib.gemv_splitk_workspace_bytes(1, 64, 65536, 4096, 0) > (8 << 20)
+    st = lib.nvfp4_gemv_splitk_noalloc(FAKE, 64, 4096, 4096, FAKE, FAKE, FAKE, 65536, 0, FAKE, None)
+    assert st == UNSUPPORTED
+    assert b"scratch" in lib.w4a16_last_error()
+    assert lib.nvfp4_gemv_splitk_noalloc(FAKE, 65, 4096, 4096, FAKE, FAKE, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
+    assert lib.nvfp4_gemv_splitk_noalloc(None, 0, 4096, 4096, None, None, None, 4096, 0, None, None) == OK

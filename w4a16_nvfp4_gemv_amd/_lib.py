@@ -21,6 +21,7 @@ SIGNATURES = {
     "gemv_splitk_workspace_bytes": (_i64, [_int, _i64, _i64, _i64, _int]),
     "nvfp4_gemv_splitk": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _i64, _p, _p]),
     "bf16_gemv_splitk": (_int, [_p, _i64, _i64, _i64, _p, _i64, _int, _p, _i64, _p, _p]),
+    "nvfp4_gemv_splitk_noalloc": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _p]),
     "dequantize_rows": (_int, [_p, _p, _i64, _i64, _p, _p]),
     "nvfp4_dequant_gemm_workspace_bytes": (_i64, [_i64, _i64, _i64]),
     "nvfp4_dequant_gemm": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _i64, _int, _p, _i64, _p, _p]),

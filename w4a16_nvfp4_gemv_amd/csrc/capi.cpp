@@ -10,6 +10,8 @@
 #include "w4a16_nvfp4_gemv.h"
 #include "launch.hpp"
 
+static_assert(W4A16_NOALLOC_SCRATCH_BYTES == w4a16::kNoAllocScratchBytes, "one scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -187,6 +189,27 @@ int nvfp4_gemv_splitk(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, cons
                       void* workspace, int64_t workspace_bytes, uint16_t* out, void* stream) {
   return run_gemv(true, x, M, K, ldx, w, w_scale, global_scale, N, silu_mul, workspace, workspace_bytes, true, out,
                   stream);
+}
+
+int nvfp4_gemv_splitk_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
+                              const uint8_t* w_scale, const float* global_scale, int64_t N, int silu_mul,
+                              uint16_t* out, void* stream) {
+  // the size checks of the GEMV entry points first (stand-in pointers), so
+  // that the plan below is computed for valid sizes only
+  const uint16_t* stand_in = reinterpret_cast<const uint16_t*>(uintptr_t(256));
+  int st = check_dense(stand_in, M, K, K, stand_in, N, silu_mul, reinterpret_cast<uint16_t*>(uintptr_t(256)), 64);
+  if (st != W4A16_OK || M == 0) return st;
+  const int64_t need = w4a16::gemv_split_plan(true, M, N, K, silu_mul).bytes;
+  if (need > W4A16_NOALLOC_SCRATCH_BYTES)
+    return fail(W4A16_ERR_UNSUPPORTED, "the split-K plan needs %lld bytes of scratch, the library holds %lld", need,
+                W4A16_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = w4a16::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return run_gemv(true, x, M, K, ldx, w, w_scale, global_scale, N, silu_mul, scratch, W4A16_NOALLOC_SCRATCH_BYTES,
+                  true, out, stream);
 }
 
 int bf16_gemv_splitk(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* w, int64_t N,

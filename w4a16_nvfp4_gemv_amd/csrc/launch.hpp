@@ -45,6 +45,11 @@ struct SplitPlan {
 constexpr int64_t kSplitCounterBytes = 65536;
 SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
 
+// The library-owned scratch of nvfp4_gemv_splitk_noalloc (noalloc.hip): its
+// device address on the current device (looked up on the first call there).
+constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream);
 // Runs the GEMV dispatch without launching: writes the name of the kernel
