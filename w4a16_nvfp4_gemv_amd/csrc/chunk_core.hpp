@@ -78,7 +78,7 @@ __device__ __forceinline__ void chunk_issue_w(ChunkW<C, R>& b, rsrc_t rw, uint32
   for (int c = 0; c < C; ++c)
 #pragma unroll
     for (int i = 0; i < R; ++i)
-      b.w[c][i] = bload4(rw, off_if(ok[c] & rv[i], static_cast<uint32_t>(rows[i]) * row_bytes + ch[c] * 4));
+      b.w[c][i] = bload4_nt(rw, off_if(ok[c] & rv[i], static_cast<uint32_t>(rows[i]) * row_bytes + ch[c] * 4));
 }
 
 // Issues the activation loads: token m's row starts at byte xoff[m] of rx

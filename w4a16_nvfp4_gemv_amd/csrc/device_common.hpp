@@ -125,6 +125,12 @@ __device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
 }
+// Streaming 4-byte variant (the VALU kernels' code loads: measured 0.2-1.1 us
+// faster per call than cached loads, which evict the scale lines and
+// activations that other workgroups still read from L2).
+__device__ __forceinline__ uint32_t bload4_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 2);
+}
 
 // 16-byte buffer load straight into LDS: lane l's 16 bytes land at byte 16*l
 // of `dst`, a wave-uniform LDS address; out-of-range dwords are written as
