@@ -6,9 +6,9 @@ One step is one pass of the dense W4A16 GEMV sweep: M in {1,2,4,8,16,32} on
 the (N, K) = (4096, 4096) and (6144, 4096) weights, 12 nvfp4_gemv calls.
 Every call reads its own copy of the weight and scales: 60 copies of each
 weight rotate (566 MB and 849 MB, each more than the 256 MB Infinity Cache),
-so weights come from HBM.  The 12 launches of a step are captured once into
-a HIP graph per copy set and replayed, so the host's launch overhead does
-not throttle the GPU.
+so weights come from HBM.  The 12 calls of a step are launched eagerly on
+one stream (the host enqueues faster than the GPU runs them); the same steps
+replayed from HIP graphs are timed beside them for comparison.
 
 value = algorithmic bytes of a step (packed weight + flat scale bytes of the
 12 calls) / wall time per step, in GB/s.  Activation and output bytes are not
@@ -16,15 +16,21 @@ counted.  Each per-call figure comes from HIP events around a graph of 64
 back-to-back launches of that one call shape on the stream the graph runs
 on.  The roofline object reports the kernel with the largest share of the
 step, with its HBM traffic from the committed rocprofv3 counter runs when
-they were taken on the current kernel sources.  The CPU baseline is the
+they were taken on the current kernel sources.  Each per-call entry also
+carries the eager-launch time of the same 64 launches and the time of a
+streaming-read reference that reads the same weight and scale copies and
+nothing else (probe/read_floor.hip), as `floor_us` and `frac_of_floor`.  The CPU baseline is the
 binary64 oracle on the host cores over whole steps of the same workload.
 The "extras" list times the other workloads of the family (fused gate|up
 SiLU GEMV, BF16-weight GEMV, MoE decode pair) the same way; they are not
 part of the step.
 
-A third helper mode times every dispatch path of the dense GEMV per token
-count (the evidence behind the fixed dispatch rule):
+A helper mode times every dispatch path of the dense GEMV per token count
+(the evidence behind the fixed dispatch rule):
     python bench.py --dispatch-table
+and one times the streaming-read reference alone over the call shapes'
+bytes and a sweep of sizes:
+    python bench.py --read-floor
 
 Two helper modes feed profiles/traffic_counters.json:
     rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --counter-pass
@@ -217,56 +223,175 @@ def graph_us_per_launch(torch, cap, launch_i, n_launch: int) -> float:
     return sorted(rounds)[1]
 
 
-DISPATCH_M = [1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64]
+def eager_us_per_launch(torch, stream, launch_i, n_launch: int) -> float:
+    """µs per launch of n_launch launches enqueued eagerly on `stream`, HIP
+    events on that stream: a sleep kernel first holds the stream while the
+    host enqueues them all, so the GPU runs them back to back whatever the
+    host's launch rate.  Median of 3 rounds after one untimed round."""
+    rounds = []
+    for r in range(4):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(max(2_000_000, 50_000 * n_launch))  # longer than the host needs to enqueue
+        a.record(stream)
+        for i in range(n_launch):
+            launch_i(i, stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            rounds.append(a.elapsed_time(b) * 1e3 / n_launch)
+    return sorted(rounds)[1]
 
 
-def dispatch_table() -> int:
-    """Per (N, K, M) of the dense sweep shapes: the µs per call of the default
-    dispatch and of each path forced with W4A16_GEMV_PATH, with the kernel
-    each one launches (graphs of 64 launches over 60 rotating weight copies,
-    timed in turns: the median of 3 rounds).  One JSON line per shape, then a
-    summary line."""
+# ---------------------------------------------------------------- read floor
+def read_floor_lib():
+    """The streaming-read reference (w4a16_nvfp4_gemv_amd/probe/read_floor.hip,
+    a library of its own beside the GEMV library)."""
+    import ctypes
+
+    from w4a16_nvfp4_gemv_amd import build_ext
+
+    if not os.path.exists(build_ext.PROBE_LIB):
+        raise SystemExit(f"{build_ext.PROBE_LIB} is not built: run python -m w4a16_nvfp4_gemv_amd.build_ext")
+    lib = ctypes.CDLL(build_ext.PROBE_LIB)
+    lib.read_floor_blocks.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.read_floor_blocks.restype = ctypes.c_int64
+    lib.read_floor_launch.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.read_floor_launch.restype = ctypes.c_int
+    return lib
+
+
+def floor_nl(nbytes: int) -> int:
+    """4 KB load rounds per workgroup so that one launch has about 256
+    workgroups (one per compute unit), at most 16."""
+    return max(1, min(16, -(-nbytes // (256 * 4096))))
+
+
+def floor_launcher(rf, torch, dev, ws, ss, w_bytes: int, s_bytes: int):
+    """launch_i(i, stream) reading copy i of (ws, ss) as the reference does."""
+    nl = floor_nl(w_bytes + s_bytes)
+    out = torch.empty(int(rf.read_floor_blocks(w_bytes, s_bytes, nl)) * 64, dtype=torch.int16, device=dev)
+    n = len(ws)
+
+    def launch(i, h):
+        st = rf.read_floor_launch(ws[i % n].data_ptr(), w_bytes, ss[i % n].data_ptr() if ss else 0,
+                                  s_bytes, nl, out.data_ptr(), h)
+        if st != 0:
+            raise RuntimeError(f"read_floor_launch failed ({st})")
+    return launch
+
+
+def read_floor_mode() -> int:
+    """Times the streaming-read reference alone: the weight + scale bytes of
+    every call shape of the benchmark and a sweep of sizes, each over rotating
+    copies (more than 600 MB) in graphs of 64 launches.  One JSON line per
+    size."""
     import torch
 
     import synth
-    from w4a16_nvfp4_gemv_amd import _lib, gemv_kernel_name
+
+    rf = read_floor_lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cap = torch.cuda.Stream()
+    sizes = [("dense 4096x4096", 4096 * 4096 // 2, synth.flat_scale_bytes(4096, 4096)),
+             ("dense 6144x4096", 6144 * 4096 // 2, synth.flat_scale_bytes(6144, 4096)),
+             ("silu 28672x4096", 28672 * 4096 // 2, synth.flat_scale_bytes(28672, 4096)),
+             ("bf16 4096x4096", 4096 * 4096 * 2, 0), ("bf16 4096x14336", 4096 * 14336 * 2, 0)]
+    sizes += [(f"{mb} MiB", mb << 20, 0) for mb in (1, 2, 4, 8, 16, 32, 64, 128)]
+    for name, wb, sb in sizes:
+        n = max(2, int(600e6 // (wb + sb)) + 1)
+        ws = [torch.randint(0, 256, (wb,), dtype=torch.uint8, device=dev) for _ in range(n)]
+        ss = [torch.randint(0, 256, (max(sb, 16),), dtype=torch.uint8, device=dev) for _ in range(n)] if sb else None
+        us = graph_us_per_launch(torch, cap, floor_launcher(rf, torch, dev, ws, ss, wb, sb), 64)
+        rec = {"read_floor": name, "bytes": wb + sb, "us": round(us, 3), "GBps": round((wb + sb) / us / 1e3, 1),
+               "frac_peak": round((wb + sb) / us / 1e3 / PEAK_GBPS, 4), "workgroups": int(rf.read_floor_blocks(wb, sb, floor_nl(wb + sb)))}
+        print(json.dumps(rec), flush=True)
+        del ws, ss
+        torch.cuda.empty_cache()
+    return 0
+
+
+DISPATCH_M = [1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64]
+# (weight, N, K, silu_mul): the sweep's weights, the fused silu call and the
+# BF16 weights of the benchmark's workloads
+DISPATCH_SHAPES = [("nvfp4", 4096, 4096, False), ("nvfp4", 6144, 4096, False), ("nvfp4", 28672, 4096, True),
+                   ("bf16", 4096, 4096, False), ("bf16", 4096, 14336, False)]
+CROSSOVER_M = [32, 48, 64, 80, 96, 128, 192, 256]
+
+
+def dispatch_table() -> int:
+    """Per (weight, N, K, silu_mul, M): µs per call of the default dispatch,
+    of each path forced with W4A16_GEMV_PATH, and of the split-K entry point
+    where its plan splits, with the kernel each one launches (graphs of 64
+    launches over rotating weight copies, timed in turns: the median of 3
+    rounds).  Then the crossover of the GEMV (up to 64 tokens) and the
+    dequant + GEMM path on the 4096 x 4096 weight (eager launches: the library
+    GEMM is not captured).  One JSON line per point, then a summary line with
+    the source digest of the kernels measured."""
+    import torch
+
+    import synth
+    from w4a16_nvfp4_gemv_amd import _lib, gemv_kernel_name, gemv_splitk_workspace
 
     lib = _lib.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cap = torch.cuda.Stream()
-    n_copies = 60
     rows, best_default = [], 0
-    for n, k, variant in SHAPES:
-        base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(1, 1, variant))
+    for wfmt, n, k, silu in DISPATCH_SHAPES:
+        fp4 = wfmt == "nvfp4"
+        base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(1, 1, n)) if fp4 else \
+            synth.dense_bf16(1, n, k, seed=synth.seed_for(3, 1, k))
+        wbytes = n * k // 2 if fp4 else n * k * 2
+        n_copies = max(2, int(600e6 // wbytes))
         ws = [base["w"].to(dev) for _ in range(n_copies)]
-        ss = [base["s"].to(dev) for _ in range(n_copies)]
+        ss = [base["s"].to(dev) for _ in range(n_copies)] if fp4 else None
         for m in DISPATCH_M:
-            d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, variant))
-            x, gs = d["x"].to(dev), d["gs"].to(dev)
-            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(1, m, n)) if fp4 else \
+                synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m, k))
+            x = d["x"].to(dev)
+            gs = d["gs"].to(dev) if fp4 else None
+            out = torch.empty((m, n // 2 if silu else n), dtype=torch.bfloat16, device=dev)
+            work = gemv_splitk_workspace(m, n, k, silu, weight_fp4=fp4, device=dev)
 
-            def launch(i, h):
-                st = lib.nvfp4_gemv(x.data_ptr(), m, k, x.stride(0), ws[i % n_copies].data_ptr(),
-                                    ss[i % n_copies].data_ptr(), gs.data_ptr(), n, 0, out.data_ptr(), h)
+            def launch(i, h, splitk=False):
+                w = ws[i % n_copies].data_ptr()
+                if fp4 and splitk:
+                    st = lib.nvfp4_gemv_splitk(x.data_ptr(), m, k, x.stride(0), w, ss[i % n_copies].data_ptr(),
+                                               gs.data_ptr(), n, int(silu), work.data_ptr(), work.numel(),
+                                               out.data_ptr(), h)
+                elif fp4:
+                    st = lib.nvfp4_gemv(x.data_ptr(), m, k, x.stride(0), w, ss[i % n_copies].data_ptr(),
+                                        gs.data_ptr(), n, int(silu), out.data_ptr(), h)
+                elif splitk:
+                    st = lib.bf16_gemv_splitk(x.data_ptr(), m, k, x.stride(0), w, n, int(silu), work.data_ptr(),
+                                              work.numel(), out.data_ptr(), h)
+                else:
+                    st = lib.bf16_gemv(x.data_ptr(), m, k, x.stride(0), w, n, int(silu), out.data_ptr(), h)
                 if st != 0:
-                    raise RuntimeError(f"nvfp4_gemv failed: {lib.w4a16_last_error().decode()}")
-            rec = {"N": n, "K": k, "M": m}
+                    raise RuntimeError(f"GEMV failed: {lib.w4a16_last_error().decode()}")
+            rec = {"weight": wfmt, "N": n, "K": k, "silu_mul": silu, "M": m}
             graphs = {}
-            for path in ("default", "valu", "mfma"):
-                if path == "default":
+            for path in ("default", "valu", "mfma", "splitk"):
+                if path in ("default", "splitk"):
                     os.environ.pop("W4A16_GEMV_PATH", None)
                 else:
                     os.environ["W4A16_GEMV_PATH"] = path
-                kern = gemv_kernel_name(m, n, k)
+                kern = gemv_kernel_name(m, n, k, silu, fp4, splitk=path == "splitk")
                 if path == "valu" and not kern.startswith(("k_gemv_vchunk", "k_gemv_valu")):
                     rec[path] = None  # no VALU kernel at this M
+                    continue
+                if path == "splitk" and kern == gemv_kernel_name(m, n, k, silu, fp4):
+                    rec[path] = None  # the plan does not split here
                     continue
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):  # the path is chosen while capturing
                     h = torch.cuda.current_stream().cuda_stream
                     for i in range(64):
-                        launch(i, h)
+                        launch(i, h, splitk=path == "splitk")
                 for _ in range(2):
                     g.replay()
                 graphs[path] = (g, kern)
@@ -293,7 +418,40 @@ def dispatch_table() -> int:
             print(json.dumps(rec), flush=True)
         del ws, ss
         torch.cuda.empty_cache()
-    print(json.dumps({"shapes": len(rows), "default_within_2pct_of_fastest_path": best_default}), flush=True)
+
+    # GEMV (to 64 tokens) against dequantize + library GEMM on 4096 x 4096
+    n, k = 4096, 4096
+    base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(5, 1))
+    n_copies = max(2, int(600e6 // (n * k // 2)))
+    ws = [base["w"].to(dev) for _ in range(n_copies)]
+    ss = [base["s"].to(dev) for _ in range(n_copies)]
+    stream = torch.cuda.Stream(device=dev)
+    cross = []
+    for m in CROSSOVER_M:
+        d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(5, m))
+        x, gs = d["x"].to(dev), d["gs"].to(dev)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        wsb = lib.nvfp4_dequant_gemm_workspace_bytes(m, n, k)
+        work = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def dq(i, h):
+            assert lib.nvfp4_dequant_gemm(x.data_ptr(), m, k, k, ws[i % n_copies].data_ptr(),
+                                          ss[i % n_copies].data_ptr(), gs.data_ptr(), n, 0, work.data_ptr(), wsb,
+                                          out.data_ptr(), h) == 0
+
+        def gv(i, h):
+            assert lib.nvfp4_gemv(x.data_ptr(), m, k, k, ws[i % n_copies].data_ptr(), ss[i % n_copies].data_ptr(),
+                                  gs.data_ptr(), n, 0, out.data_ptr(), h) == 0
+        rec = {"crossover": "4096x4096", "M": m,
+               "dequant_gemm_us": round(eager_us_per_launch(torch, stream, dq, 32), 3)}
+        if m <= 64:
+            rec["gemv_us"] = round(eager_us_per_launch(torch, stream, gv, 32), 3)
+            rec["gemv_kernel"] = gemv_kernel_name(m, n, k)
+        cross.append(rec)
+        print(json.dumps(rec), flush=True)
+    print(json.dumps({"points": len(rows), "default_within_2pct_of_fastest_path": best_default,
+                      "gemv_wins_to_64_tokens": all(r["gemv_us"] < r["dequant_gemm_us"] for r in cross if "gemv_us" in r),
+                      "source_digest": source_digest()}), flush=True)
     return 0
 
 
@@ -310,6 +468,7 @@ def main() -> int:
     ap.add_argument("--counter-pass", action="store_true")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--dispatch-table", action="store_true")
+    ap.add_argument("--read-floor", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
@@ -319,6 +478,8 @@ def main() -> int:
         return ingest_counters(*args.ingest_counters)
     if args.dispatch_table:
         return dispatch_table()
+    if args.read_floor:
+        return read_floor_mode()
 
     import torch
 
@@ -371,11 +532,39 @@ def main() -> int:
     log(f"weight copies resident: {resident / 1e6:.0f} MB")
     step_bytes = sum(algorithmic_bytes(c["n"], c["k"]) for c in calls)
 
-    # ---------------------------------------------------------------- graphs
+    # ---------------------------------------------------------------- timed steps
+    # The 12 calls of a step are launched eagerly on one stream, copy set
+    # after copy set.  Measured on this stack: the same steps replayed as HIP
+    # graphs take ~6 us more per step (a graph of one kernel repeated costs
+    # what eager launches cost, a graph of 12 different kernels ~0.4 us more
+    # per node), and the host enqueues a step faster than the GPU runs it.
     cap = torch.cuda.Stream()
-    for c in calls:  # eager run on the capture stream: every call is accepted
+    for c in calls:  # every call is accepted
         launch(c, 0, cap.cuda_stream)
     torch.cuda.synchronize()
+
+    def run_step(i):
+        cs = i % COPY_SETS
+        for c in calls:
+            launch(c, cs * len(SWEEP_M) + c["j"], cap.cuda_stream)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(cap)
+    for i in range(args.steps):
+        run_step(i)
+    ev1.record(cap)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_ms * 1e3 / args.steps:.2f} us/step events")
+
+    # the same steps replayed from HIP graphs (one per copy set), for comparison
     graphs = []
     for cs in range(COPY_SETS):
         g = torch.cuda.CUDAGraph()
@@ -384,24 +573,19 @@ def main() -> int:
             for c in calls:
                 launch(c, cs * len(SWEEP_M) + c["j"], h)
         graphs.append(g)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- timed steps
-    for i in range(args.warmup):
+    for i in range(2 * COPY_SETS):
         graphs[i % COPY_SETS].replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
+    graph_steps = min(args.steps, 100)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(graph_steps):
         graphs[i % COPY_SETS].replay()
-    ev1.record()
+    e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall * 1e3 / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"{args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, {gpu_ms * 1e3 / args.steps:.2f} us/step events")
+    graph_us = e0.elapsed_time(e1) * 1e3 / graph_steps
+    del graphs
+    log(f"graph replay: {graph_us:.2f} us/step")
 
     # ---------------------------------------------------------------- per call
     def time_graph(launch_i, n_launch: int) -> float:
@@ -409,13 +593,24 @@ def main() -> int:
 
     per_call = []
     L = args.per_call_launches
+    rf = read_floor_lib()
+    floors = {}
     for c in calls:
         us = time_graph(lambda i, h, c=c: launch(c, i % n_copies, h), L)
         nbytes = algorithmic_bytes(c["n"], c["k"])
+        us_eager = eager_us_per_launch(torch, cap, lambda i, h, c=c: launch(c, i % n_copies, h), L)
+        key = (c["n"], c["k"])
+        if key not in floors:
+            # the streaming-read reference over the same weight and scale copies
+            floors[key] = time_graph(floor_launcher(rf, torch, dev, c["w"], c["s"], c["n"] * c["k"] // 2,
+                                                    c["s"][0].numel()), L)
         per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": c["kernel"],
                          "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
-                         "frac_peak": round(nbytes / us / 1e3 / PEAK_GBPS, 4), "bytes": nbytes})
-        log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s  {c['kernel']}")
+                         "frac_peak": round(nbytes / us / 1e3 / PEAK_GBPS, 4), "bytes": nbytes,
+                         "floor_us": round(floors[key], 3), "frac_of_floor": round(floors[key] / us, 4),
+                         "us_eager": round(us_eager, 3)})
+        log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s  "
+            f"(eager {us_eager:.3f} us, read floor {floors[key]:.3f} us)  {c['kernel']}")
 
     # dominant kernel: largest share of the step's time
     share = {}
@@ -435,7 +630,6 @@ def main() -> int:
                 "kernel": dom, "avg_us_per_launch": round(avg_us, 3),
                 "algorithmic_bytes_per_launch": int(avg_bytes), "launches_per_step": d["launches"],
                 "step_time_share": round(d["us"] / sum(pc["us"] for pc in per_call), 3)}
-    del graphs
     for c in calls:
         c["w"] = c["s"] = None
     torch.cuda.empty_cache()
@@ -467,6 +661,9 @@ def main() -> int:
                    "weight_copies_MB": round(resident / 1e6)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "step_launch": {"eager_us_per_step": round(gpu_ms * 1e3 / args.steps, 2),
+                        "graph_replay_us_per_step": round(graph_us, 2),
+                        "sum_of_per_call_us": round(sum(pc["us"] for pc in per_call), 2)},
         "per_call": per_call,
         "extras": extras,
         "source_digest": source_digest(),
@@ -531,31 +728,111 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
     w2_e = H * I // 2 + synth.flat_scale_bytes(H, I)
     sh1 = 2 * SI * H // 2 + synth.flat_scale_bytes(2 * SI, H)
     sh2 = H * SI // 2 + synth.flat_scale_bytes(H, SI)
+    # 16 copies of the shared expert rotate with the routings, and at one
+    # token the 16 routings take 16 disjoint sets of 8 experts (a seeded
+    # random partition of the 128): between two reads of any expert, about
+    # 1.4 GB of other weights stream through, more than the 256 MB Infinity
+    # Cache holds.  At 8 and 32 tokens a call reads 52 / 112 of the 128
+    # experts (1.36 GB in all), so fresh random routings suffice.
+    shared = [{k2: wts[k2] if j == 0 else wts[k2].clone() for k2 in ("wsh", "ssh", "wsd", "ssd")} for j in range(16)]
+    part = torch.randperm(E, generator=torch.Generator().manual_seed(synth.seed_for(4, 1, 9))).view(-1, T)
     for m in (1, 8, 32):
         sets = []
-        for r in range(16):  # rotating routings: fresh experts every launch
+        for r in range(16):
             tk = synth.moe_tokens(m, H, E, T, seed=synth.seed_for(4, m, r))
+            if m == 1:
+                tk["ids"] = part[r % part.shape[0]].view(1, T).to(torch.int32).contiguous()
             sets.append({k2: v.to(dev) for k2, v in tk.items()})
         act = torch.empty((m * T, I), dtype=torch.bfloat16, device=dev)
         sact = torch.empty((m, SI), dtype=torch.bfloat16, device=dev)
         o = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
 
         def gu(i, h, sets=sets, act=act, sact=sact):
-            t = sets[i % len(sets)]
-            moe_gate_up(t["x"], t["ids"], wts["w1"], wts["w1_sf"], wts["alpha"], act, wts["wsh"], wts["ssh"],
+            t, sh = sets[i % len(sets)], shared[i % len(shared)]
+            moe_gate_up(t["x"], t["ids"], wts["w1"], wts["w1_sf"], wts["alpha"], act, sh["wsh"], sh["ssh"],
                         wts["gssh"], sact)
 
         def dc(i, h, sets=sets, act=act, sact=sact, o=o):
-            t = sets[i % len(sets)]
-            moe_down_combine(act, t["ids"], t["tw"], wts["w2"], wts["w2_sf"], wts["alpha2"], sact, wts["wsd"],
-                             wts["ssd"], wts["gssd"], o)
+            t, sh = sets[i % len(sets)], shared[i % len(shared)]
+            moe_down_combine(act, t["ids"], t["tw"], wts["w2"], wts["w2_sf"], wts["alpha2"], sact, sh["wsd"],
+                             sh["ssd"], wts["gssd"], o)
+
+        def pair(i, h):
+            gu(i, h)
+            dc(i, h)
         distinct = sum(len(set(t["ids"].flatten().tolist())) for t in sets) / len(sets)
         for name, fn, nb in (("moe_gate_up", gu, distinct * w1_e + sh1), ("moe_down_combine", dc, distinct * w2_e + sh2)):
             us = time_graph(fn, 32)
             out.append({"workload": name, "M": m, "experts_per_call": round(distinct, 2), "us": round(us, 3),
                         "GBps": round(nb / us / 1e3, 1), "bytes": int(nb)})
             log(f"{name} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s ({distinct:.1f} experts)")
-    del wts
+        # the pair in one graph, and launched eagerly from the host
+        us_graph = time_graph(pair, 32)
+        stream = torch.cuda.current_stream()
+        for i in range(4):
+            pair(i, stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(64):
+            pair(i, stream.cuda_stream)
+        e1.record()
+        torch.cuda.synchronize()
+        us_eager = e0.elapsed_time(e1) * 1e3 / 64
+        nb = distinct * (w1_e + w2_e) + sh1 + sh2
+        out.append({"workload": "moe pair", "M": m, "us_graph": round(us_graph, 3), "us_eager": round(us_eager, 3),
+                    "GBps_graph": round(nb / us_graph / 1e3, 1), "bytes": int(nb)})
+        log(f"moe pair M={m:2d}: {us_graph:7.3f} us in a graph, {us_eager:7.3f} us launched eagerly")
+    del wts, shared
+
+    # The split-K entry points (a caller workspace) against the ones without,
+    # at shapes whose plan splits: the BF16 weight with K = 14336, NVFP4 with
+    # K = 14336, and narrow weights whose row tiles fill few compute units.
+    from w4a16_nvfp4_gemv_amd import gemv_splitk_workspace
+    for fp4, n, k, ms in ((False, 4096, 14336, (16, 32)), (True, 4096, 14336, (16, 32)),
+                          (True, 1024, 8192, (4, 16, 32)), (False, 2048, 8192, (4, 32))):
+        base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(8, 1, n)) if fp4 else \
+            synth.dense_bf16(1, n, k, seed=synth.seed_for(8, 1, n))
+        wbytes = n * k // 2 if fp4 else n * k * 2
+        nc = max(2, int(budget // wbytes))
+        ws = [base["w"].to(dev) for _ in range(nc)]
+        ss = [base["s"].to(dev) for _ in range(nc)] if fp4 else None
+        nb = algorithmic_bytes(n, k) if fp4 else wbytes
+        for m in ms:
+            d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(8, m, n)) if fp4 else \
+                synth.dense_bf16(m, n, k, seed=synth.seed_for(8, m, n))
+            x = d["x"].to(dev)
+            gs = d["gs"].to(dev) if fp4 else None
+            o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            work = gemv_splitk_workspace(m, n, k, weight_fp4=fp4, device=dev)
+            rec = {"workload": ("nvfp4" if fp4 else "bf16") + "_gemv_splitk", "N": n, "K": k, "M": m, "bytes": nb,
+                   "kernel": gemv_kernel_name(m, n, k, weight_fp4=fp4, splitk=True),
+                   "kernel_without_workspace": gemv_kernel_name(m, n, k, weight_fp4=fp4)}
+            entries = ["plain", "splitk"] + (["noalloc"] if fp4 else [])
+            for entry in entries:
+                def f(i, h, entry=entry, m=m, x=x, gs=gs, o=o, n=n, k=k, work=work, fp4=fp4):
+                    w = ws[i % nc].data_ptr()
+                    if fp4 and entry == "plain":
+                        st = lib.nvfp4_gemv(x.data_ptr(), m, k, k, w, ss[i % nc].data_ptr(), gs.data_ptr(), n, 0,
+                                            o.data_ptr(), h)
+                    elif fp4 and entry == "splitk":
+                        st = lib.nvfp4_gemv_splitk(x.data_ptr(), m, k, k, w, ss[i % nc].data_ptr(), gs.data_ptr(), n,
+                                                   0, work.data_ptr(), work.numel(), o.data_ptr(), h)
+                    elif fp4:
+                        st = lib.nvfp4_gemv_splitk_noalloc(x.data_ptr(), m, k, k, w, ss[i % nc].data_ptr(),
+                                                           gs.data_ptr(), n, 0, o.data_ptr(), h)
+                    elif entry == "plain":
+                        st = lib.bf16_gemv(x.data_ptr(), m, k, k, w, n, 0, o.data_ptr(), h)
+                    else:
+                        st = lib.bf16_gemv_splitk(x.data_ptr(), m, k, k, w, n, 0, work.data_ptr(), work.numel(),
+                                                  o.data_ptr(), h)
+                    assert st == 0, lib.w4a16_last_error()
+                rec["us_" + entry] = round(time_graph(f, 32), 3)
+            rec["GBps"] = round(nb / rec["us_splitk"] / 1e3, 1)
+            out.append(rec)
+            log(f"{rec['workload']} N={n} K={k} M={m:2d}: {rec['us_plain']:7.3f} us -> {rec['us_splitk']:7.3f} us "
+                f"with a workspace ({rec['kernel']})")
+        del ws, ss
 
     # The MFMA GEMV past 32 tokens (up to four 16-token tiles)
     for n, k in ((4096, 4096), (6144, 4096)):

@@ -31,6 +31,27 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+PROBE = os.path.join(HERE, "probe", "read_floor.hip")
+PROBE_LIB = os.path.join(HERE, "libw4a16_read_floor.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The streaming-read reference the benchmark times beside the GEMV (a
+    library of its own: nothing in the GEMV library uses it)."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+           PROBE, "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -59,3 +80,4 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
