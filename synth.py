@@ -60,12 +60,31 @@ def flat_scales(n: int, k: int, g: torch.Generator) -> torch.Tensor:
                          generator=g, dtype=torch.uint8)
 
 
-def dense_w4a16(m: int, n: int, k: int, seed: int) -> dict:
-    """x bf16 [m, k], w uint8 [n, k/2], s uint8 flat swizzled, gs fp32 [1]."""
+def flat_scales_all_finite(n: int, k: int, g: torch.Generator) -> torch.Tensor:
+    """Scale bytes uniform over all 254 finite E4M3FN codes: zero and
+    subnormal codes (0x00-0x07), normal ones up to 448 (0x7E), and all their
+    negatives (0x80-0xFE); the two NaN codes 0x7F / 0xFF are left out."""
+    codes = torch.randint(0, 254, (flat_scale_bytes(n, k),), generator=g, dtype=torch.int32)
+    codes = codes + (codes >= 0x7F).to(torch.int32)          # skip 0x7F
+    return codes.to(torch.uint8)
+
+
+def activations_wide(m: int, k: int, g: torch.Generator, lo: int, hi: int) -> torch.Tensor:
+    """N(0, 1) values each multiplied by 2^e, e uniform over [lo, hi],
+    rounded to BF16 (lo <= -127 reaches BF16 subnormals)."""
+    x = torch.randn((m, k), generator=g, dtype=torch.float64)
+    e = torch.randint(lo, hi + 1, (m, k), generator=g, dtype=torch.int64)
+    return (x * torch.pow(2.0, e.to(torch.float64))).to(torch.float32).to(torch.bfloat16)
+
+
+def dense_w4a16(m: int, n: int, k: int, seed: int, scales: str = "config", x_exp: tuple | None = None) -> dict:
+    """x bf16 [m, k], w uint8 [n, k/2], s uint8 flat swizzled, gs fp32 [1].
+    scales="all_finite" draws every finite E4M3 code (edge-case tests);
+    x_exp=(lo, hi) scales each activation by 2^e, e uniform over [lo, hi]."""
     g = _gen(seed)
-    x = activations(m, k, g)
+    x = activations(m, k, g) if x_exp is None else activations_wide(m, k, g, *x_exp)
     w = packed_weight(n, k, g)
-    s = flat_scales(n, k, g)
+    s = flat_scales(n, k, g) if scales == "config" else flat_scales_all_finite(n, k, g)
     gs = torch.tensor([GLOBAL_SCALE], dtype=torch.float32)
     return dict(x=x, w=w, s=s, gs=gs)
 
@@ -92,21 +111,30 @@ def moe_alphas(n_experts: int):
     return alpha, alpha2
 
 
-def moe_weights(n_experts: int, hidden: int, inter: int, shared_inter: int, seed: int) -> dict:
+def moe_weights(n_experts: int, hidden: int, inter: int, shared_inter: int, seed: int,
+                scales: str = "config") -> dict:
     """Routed W1 [E, 2I, H/2] + flat scales [E, bytes(2I, H)], W2 [E, H, I/2] +
     flat scales [E, bytes(H, I)], shared Wsh [2SI, H/2] / Wsd [H, SI/2] with
-    flat scales, per-expert alphas and the shared global scales."""
+    flat scales, per-expert alphas and the shared global scales
+    (scales="all_finite": every finite E4M3 code, as dense_w4a16)."""
     g = _gen(seed)
+
+    def expert_scales(rows, cols):
+        if scales == "config":
+            return torch.randint(SCALE_CODE_LO, SCALE_CODE_HI + 1, (n_experts, flat_scale_bytes(rows, cols)),
+                                 generator=g, dtype=torch.uint8)
+        return torch.stack([flat_scales_all_finite(rows, cols, g) for _ in range(n_experts)])
+
+    def one_scales(rows, cols):
+        return flat_scales(rows, cols, g) if scales == "config" else flat_scales_all_finite(rows, cols, g)
     w1 = torch.randint(0, 256, (n_experts, 2 * inter, hidden // 2), generator=g, dtype=torch.uint8)
-    w1_sf = torch.randint(SCALE_CODE_LO, SCALE_CODE_HI + 1,
-                          (n_experts, flat_scale_bytes(2 * inter, hidden)), generator=g, dtype=torch.uint8)
+    w1_sf = expert_scales(2 * inter, hidden)
     w2 = torch.randint(0, 256, (n_experts, hidden, inter // 2), generator=g, dtype=torch.uint8)
-    w2_sf = torch.randint(SCALE_CODE_LO, SCALE_CODE_HI + 1,
-                          (n_experts, flat_scale_bytes(hidden, inter)), generator=g, dtype=torch.uint8)
+    w2_sf = expert_scales(hidden, inter)
     wsh = packed_weight(2 * shared_inter, hidden, g)
-    ssh = flat_scales(2 * shared_inter, hidden, g)
+    ssh = one_scales(2 * shared_inter, hidden)
     wsd = packed_weight(hidden, shared_inter, g)
-    ssd = flat_scales(hidden, shared_inter, g)
+    ssd = one_scales(hidden, shared_inter)
     alpha, alpha2 = moe_alphas(n_experts)
     gssh = torch.tensor([GLOBAL_SCALE], dtype=torch.float32)
     gssd = torch.tensor([GLOBAL_SCALE], dtype=torch.float32)

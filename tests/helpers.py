@@ -122,12 +122,14 @@ def dequant_reference(w, flat, n: int, k: int) -> np.ndarray:
 
 # ---------------------------------------------------------------- bounds
 def ulp_bf16(v) -> np.ndarray:
-    """Spacing of BF16 numbers at |v|: 2^(max(floor(log2|v|), -126) - 7)."""
+    """Spacing of BF16 numbers at |v|: 2^(max(floor(log2|v|), -126) - 7)
+    (infinite for infinite or NaN v: such values are compared exactly)."""
     a = np.abs(np.asarray(v, np.float64))
+    fin = np.isfinite(a)
     with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        e = np.floor(np.log2(np.where((a > 0) & fin, a, 1.0)))
     e = np.where(a > 0, np.maximum(e, -126), -126)
-    return np.ldexp(1.0, (e - 7).astype(np.int64))
+    return np.where(fin, np.ldexp(1.0, (e - 7).astype(np.int64)), np.inf)
 
 
 def gemv_bound(ref_value, absacc, gs) -> np.ndarray:
@@ -158,8 +160,9 @@ def silu_bound(out_ref, g, u, bg, bu) -> np.ndarray:
 def assert_close_bits(got_bits, want_bits, bound, what: str, nan_ok: bool = False):
     got = bf16_bits_to_f64(got_bits)
     want = bf16_bits_to_f64(want_bits)
-    both_nan = np.isnan(got) & np.isnan(want)
-    diff = np.where(both_nan, 0.0, np.abs(got - want))
+    same = (np.isnan(got) & np.isnan(want)) | (got == want)   # includes equal infinities
+    with np.errstate(invalid="ignore"):
+        diff = np.where(same, 0.0, np.abs(got - want))
     bad = ~(diff <= bound)
     if bad.any():
         idx = np.argwhere(bad)[:8]
