@@ -90,6 +90,19 @@ struct alignas(16) MoeRouting {
   int32_t D;                        // distinct experts
 };
 
+// The routing the VALU forms need for their at most 2 x 16 pairs (the fields
+// of MoeRouting they read), about 0.7 KB of LDS instead of 26 KB, so that
+// LDS does not bound how many of their workgroups a compute unit holds.
+constexpr int kMoeValuMaxPairs = 32;
+struct alignas(16) MoeRoutingSmall {
+  int32_t expert[kMoeValuMaxPairs];
+  int32_t count[kMoeValuMaxPairs];
+  int32_t start[kMoeValuMaxPairs + 1];
+  int32_t order[kMoeValuMaxPairs];
+  float tw[kMoeValuMaxPairs];
+  int32_t D;
+};
+
 // Number of i in [lo, hi) with a[i] == v: a scan of an LDS array in blocks of
 // 16 entries read as four 16-byte broadcasts (the array is readable up to
 // kMoeMaxPairs; entries outside [lo, hi) are masked).
@@ -194,6 +207,60 @@ __device__ void build_routing(MoeRouting& r, const int32_t* ids, const float* tw
   __syncthreads();
 }
 
+// The same routing for at most 64 pairs (one per lane of the first wave),
+// with cross-lane reads instead of LDS tables: the other waves only wait at
+// the closing barrier.  The VALU forms (one or two tokens: at most 32 pairs)
+// use it; a decode step's few pairs then cost a handful of scalar loops
+// instead of the table passes and their barriers (measured 0.5 / 0.8 us off
+// gate_up / down_combine at one token).  The MFMA forms keep the table
+// builder: with both builders in them they ran 12-16% slower at 8 and 32
+// tokens.
+template <typename Routing>
+__device__ void build_routing_wave(Routing& r, const int32_t* ids, const float* tw, int P, int E) {
+  if (threadIdx.x < 64) {
+    const int p = threadIdx.x;
+    const bool live = p < P;
+    // absent pairs get distinct negative ids, so they match nothing
+    const int e = live ? clamp_expert(ids[p], E) : -1 - p;
+    int first = p, within = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      if (q < p && eq == e) {
+        ++within;
+        first = q < first ? q : first;
+      }
+    }
+    const bool is_first = live && first == p;
+    const uint64_t firsts = __ballot(is_first);
+    const int slot_if_first = __popcll(firsts & ((uint64_t(1) << p) - 1));
+    int count = 0;
+    for (int q = 0; q < P; ++q) count += __builtin_amdgcn_readlane(first, q) == p ? 1 : 0;
+    // start of a first pair's slot: the counts of the first pairs before it
+    int start = 0;
+    for (int q = 0; q < P; ++q) {  // a uniform loop: q is the same on every lane
+      const int fq = __builtin_amdgcn_readlane(first, q);
+      const int cq = __builtin_amdgcn_readlane(count, q);
+      start += (q < p && fq == q) ? cq : 0;
+    }
+    const int my_start = __shfl(start, first);
+    if (is_first) {
+      r.expert[slot_if_first] = e;
+      r.count[slot_if_first] = count;
+      r.start[slot_if_first] = start;
+    }
+    if (live) {
+      r.order[my_start + within] = p;
+      if (tw) r.tw[p] = tw[p];
+    }
+    if (p == 0) {
+      r.D = __popcll(firsts);
+      r.start[__popcll(firsts)] = P;
+    }
+  }
+  __syncthreads();
+}
+
+
 // ------------------------------------------------------------------ gate_up
 // Work items are (slot, gate quad of the expert's I rows) and (gate quad of
 // the shared expert's SI rows); a persistent grid builds the routing once per
@@ -208,13 +275,13 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
   constexpr int PV = 2;                 // gate, up
   constexpr int V = MT * 4 * PV;        // value index (m * 4 + q) * 2 + u
   using RS = ReduceScatter<V, PV>;
-  __shared__ MoeRouting rt;
+  __shared__ MoeRoutingSmall rt;
   __shared__ float red[KS - 1][RS::LEFT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kw = uniform(tid >> 6);
-  const int P = p.M * p.topk;
-  build_routing(rt, p.ids, nullptr, P, p.E);
+  const int P = p.M * p.topk;  // at most 2 x 16: one wave builds the routing
+  build_routing_wave(rt, p.ids, nullptr, P, p.E);
   const int D = uniform(rt.D);
   // 32-bit item bookkeeping: at most 512 slots x (I / 4) quads
   const int units_r = (p.I + 127) / 128 * 32;
@@ -319,18 +386,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
 }
 
 // ------------------------------------------------------------------ down_combine
-template <int MT, int C>
-__global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p) {
+template <int MT, int C, int NW>
+__global__ __launch_bounds__(NW * 64) void k_moe_down_combine(const MoeDownParams p) {
   constexpr int V = MT * 4;  // value index m * 4 + q
   using RS = ReduceScatter<V, 1>;
-  __shared__ MoeRouting rt;
-  __shared__ float part[4][kMoeMaxTokens][4];
+  __shared__ MoeRoutingSmall rt;
+  __shared__ float part[NW][kMoeMaxTokens][4];
   __shared__ float ysh[kMoeMaxTokens][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int P = p.M * p.topk;
-  build_routing(rt, p.ids, p.tw, P, p.E);
+  const int P = p.M * p.topk;  // at most 2 x 16: one wave builds the routing
+  build_routing_wave(rt, p.ids, p.tw, P, p.E);
   const int D = uniform(rt.D);
   const float gssd = *p.gssd;
   const int64_t units = (p.H + 127) / 128 * 32;
@@ -339,7 +406,7 @@ __global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p)
   const uint32_t sact_bytes = static_cast<uint32_t>(p.M) * p.SI * 2;
 
   // Job = (slot s, group of MT tokens from g0, K block kb); wave w takes the
-  // slots s = w, w + 4, ...; slot D is the shared expert.
+  // slots s = w, w + NW, ...; slot D is the shared expert.
   struct Job {
     int s, g0, kb;
   };
@@ -357,13 +424,13 @@ __global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p)
       j.g0 += MT;
       if (j.g0 >= npairs_of(j.s)) {
         j.g0 = 0;
-        j.s += 4;
+        j.s += NW;
       }
     }
     return j;
   };
   int njobs = 0;
-  for (int s = wave; s <= D; s += 4) njobs += (npairs_of(s) + MT - 1) / MT * nkb_of(s);
+  for (int s = wave; s <= D; s += NW) njobs += (npairs_of(s) + MT - 1) / MT * nkb_of(s);
 
   for (int64_t u = xcd_logical_block(); u < units; u += gridDim.x) {
     int64_t rows[4];
@@ -472,7 +539,9 @@ __global__ __launch_bounds__(256) void k_moe_down_combine(const MoeDownParams p)
       const int t = i >> 2, q = i & 3;
       const int64_t row = (u >> 5) * 128 + (u & 31) + 32 * q;
       if (row < p.H) {
-        const float s = ((part[0][t][q] + part[1][t][q]) + part[2][t][q]) + part[3][t][q];
+        float s = part[0][t][q];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) s += part[w][t][q];  // in wave order
         const float sr = bf16_bits_to_f32(f32_to_bf16_bits(s));
         p.out[static_cast<int64_t>(t) * p.H + row] = f32_to_bf16_bits(sr + ysh[t][q]);
       }
@@ -914,15 +983,19 @@ hipError_t launch_gate_up_mt(const MoeGateUpParams& p, int c, hipStream_t stream
   return hipGetLastError();
 }
 
+// Waves per down_combine workgroup (each takes every kMoeDownValuWaves-th slot).
+constexpr int kMoeDownValuWaves = 4;
+
 template <int MT>
 hipError_t launch_down_mt(const MoeDownParams& p, int c, hipStream_t stream) {
+  constexpr int NW = kMoeDownValuWaves;
   const int64_t units = (p.H + 127) / 128 * 32;
-  const dim3 grid(static_cast<unsigned>(units < 4096 ? units : 4096)), block(256);
+  const dim3 grid(static_cast<unsigned>(units < 4096 ? units : 4096)), block(NW * 64);
   switch (c) {
-    case 1: hipLaunchKernelGGL((k_moe_down_combine<MT, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_moe_down_combine<MT, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((k_moe_down_combine<MT, 3>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_moe_down_combine<MT, 4>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((k_moe_down_combine<MT, 1, NW>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_moe_down_combine<MT, 2, NW>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((k_moe_down_combine<MT, 3, NW>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((k_moe_down_combine<MT, 4, NW>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }
@@ -942,8 +1015,9 @@ int chunks_per_lane(int64_t k, int64_t lanes, int cmax) {
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   const int pairs = p.M * p.topk;
   p.slots_max = pairs < p.E ? pairs : p.E;
-  // (the VALU forms read a quad's scale words as one 16-byte chunk)
-  if (moe_use_mfma(p.M) || !p.scales16) {
+  // (the VALU forms read a quad's scale words as one 16-byte chunk, and
+  // route at most kMoeValuMaxPairs pairs)
+  if (moe_use_mfma(p.M) || !p.scales16 || pairs > kMoeValuMaxPairs) {
     // one work unit per wave at least, two resident workgroups per CU at most
     const int64_t units = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 8) + (p.SI + 127) / 128 * 8;
     int64_t blocks = (units + kMoeGateUpWaves - 1) / kMoeGateUpWaves;
@@ -959,7 +1033,7 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
 }
 
 hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
-  if (moe_use_mfma(p.M) || !p.scales16) {
+  if (moe_use_mfma(p.M) || !p.scales16 || p.M * p.topk > kMoeValuMaxPairs) {
     const int64_t tiles = (p.H + 127) / 128 * 8;
     const dim3 grid(static_cast<unsigned>(tiles < 4096 ? tiles : 4096)), block(kMoeDownWaves * 64);
     if (p.M <= 4) hipLaunchKernelGGL((k_moe_down_mfma<4>), grid, block, 0, stream, p);
