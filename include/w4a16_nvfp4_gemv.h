@@ -29,9 +29,10 @@
  * the FP32 accumulator and the result is rounded to BF16 once (round to
  * nearest even).  The FP32 summation order is unspecified.
  *
- * Shape limits shared by the GEMV entry points: 0 <= M <= 64 tokens (M == 0
- * is a successful no-op; the pages' kernels stop at 32 tokens, the MFMA
- * kernels here take up to four 16-token tiles), K % 64 == 0, N % 16 == 0, all sizes below 2^31.
+ * Shape limits shared by the GEMV entry points: 0 <= M <= W4A16_MAX_M tokens
+ * (M == 0 is a successful no-op; the pages' kernels stop at 32 tokens, the
+ * MFMA kernels here take up to four 16-token tiles per launch), K % 64 == 0,
+ * N % 16 == 0, all sizes below 2^31.
  * Pointer alignment: activations and weights 16 bytes, scale buffers and
  * global scales 4 bytes (one 32-bit word holds a row's 4 scales of a 64-k
  * tile: the 4-byte divisibility of the moe_gemv page's fake tensor specs),
@@ -60,8 +61,12 @@ extern "C" {
 #define W4A16_ERR_UNSUPPORTED 3   /* valid request outside the supported shapes */
 #define W4A16_ERR_HIP 4           /* the HIP runtime refused a launch */
 
-/* Largest token count of the GEMV entry points, and of the MoE pair. */
-#define W4A16_MAX_M 64
+/* Largest token count of the GEMV entry points, and of the MoE pair.  The
+ * GEMV kernels take up to 64 tokens per launch; from 65 tokens on a call
+ * launches them once per 64 tokens (each launch reads the weight again),
+ * which measured faster than the dequant + GEMM path up to 192 tokens. */
+#define W4A16_MAX_M 192
+#define W4A16_GEMV_TOKENS_PER_LAUNCH 64
 #define W4A16_MOE_MAX_M 32
 
 /*

@@ -63,7 +63,7 @@ def gemv(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(M=65), UNSUPPORTED),
+    (dict(M=193), UNSUPPORTED),
     (dict(M=-1), INVALID),
     (dict(K=4032 + 32), UNSUPPORTED),    # K % 64 != 0
     (dict(K=0), INVALID),
@@ -92,7 +92,7 @@ def test_nvfp4_gemv_argument_errors(kw, status):
 
 def test_bf16_gemv_argument_errors():
     lib = _lib.load()
-    assert lib.bf16_gemv(FAKE, 65, 4096, 4096, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
+    assert lib.bf16_gemv(FAKE, 193, 4096, 4096, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
     assert lib.bf16_gemv(FAKE, 1, 4104, 4104, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED  # K % 16
     assert lib.bf16_gemv(FAKE, 0, 4096, 4096, None, 4096, 0, None, None) == OK
 
@@ -213,7 +213,10 @@ def test_gemv_kernel_name_query(monkeypatch):
     assert gemv_kernel_name(4, 4096, 4096).startswith("k_gemv_vchunk<4, false,")
     assert gemv_kernel_name(64, 6144, 4096).endswith(", 2, 1>")  # two row tiles per workgroup
     assert gemv_kernel_name(64, 2 * 6144, 4096, silu_mul=True).endswith(", 1, 1>")  # LDS: one with silu_mul
-    for bad in (dict(m=0, n=16, k=64), dict(m=65, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
+    # past 64 tokens a call launches the 64-token kernel once per 64 tokens
+    assert gemv_kernel_name(192, 4096, 4096) == gemv_kernel_name(64, 4096, 4096)
+    assert gemv_kernel_name(100, 6144, 4096) == gemv_kernel_name(64, 6144, 4096)
+    for bad in (dict(m=0, n=16, k=64), dict(m=193, n=16, k=64), dict(m=1, n=16, k=60), dict(m=1, n=8, k=64)):
         with pytest.raises(W4A16Error):
             gemv_kernel_name(bad["m"], bad["n"], bad["k"])
 
@@ -254,7 +257,9 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
     assert gemv_kernel_name(16, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 16, false, 1, 1>"
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False, splitk=True) == "k_gemv_mfma<false, 32, false, 2, 2>"
     assert gemv_kernel_name(32, 4096, 4096, silu_mul=True, splitk=True) == "k_gemv_mfma<true, 32, true, 1, 2>"
-    assert lib.gemv_splitk_workspace_bytes(1, 65, 4096, 4096, 0) == -1
+    assert lib.gemv_splitk_workspace_bytes(1, 193, 4096, 4096, 0) == -1
+    # past 64 tokens: the plan of the 64-token launches
+    assert lib.gemv_splitk_workspace_bytes(1, 192, 1024, 8192, 0) == lib.gemv_splitk_workspace_bytes(1, 64, 1024, 8192, 0)
     assert lib.gemv_splitk_workspace_bytes(2, 32, 4096, 4096, 0) == -1
     monkeypatch.setenv("W4A16_SPLITK", "off")
     assert lib.gemv_splitk_workspace_bytes(1, 32, 1024, 8192, 0) == 0
@@ -269,7 +274,7 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
     (dict(ws=None), INVALID),                 # the plan splits: a workspace is needed
     (dict(wsb=4096), INVALID),                # too small
     (dict(ws=FAKE + 64), MISALIGNED),         # 256-byte alignment
-    (dict(M=65), UNSUPPORTED),
+    (dict(M=193), UNSUPPORTED),
     (dict(s=FAKE + 2), MISALIGNED),
     (dict(M=0, x=None, w=None, s=None, gs=None, ws=None, out=None), OK),
 ])
@@ -301,5 +306,5 @@ def test_noalloc_rejects_plans_beyond_its_scratch(monkeypatch):
     st = lib.nvfp4_gemv_splitk_noalloc(FAKE, 64, 4096, 4096, FAKE, FAKE, FAKE, 65536, 0, FAKE, None)
     assert st == UNSUPPORTED
     assert b"scratch" in lib.w4a16_last_error()
-    assert lib.nvfp4_gemv_splitk_noalloc(FAKE, 65, 4096, 4096, FAKE, FAKE, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
+    assert lib.nvfp4_gemv_splitk_noalloc(FAKE, 193, 4096, 4096, FAKE, FAKE, FAKE, 4096, 0, FAKE, None) == UNSUPPORTED
     assert lib.nvfp4_gemv_splitk_noalloc(None, 0, 4096, 4096, None, None, None, 4096, 0, None, None) == OK

@@ -139,6 +139,47 @@ def test_nvfp4_gemv_up_to_64_tokens(m, n, k, silu):
         check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [65, 100, 128, 192])
+@pytest.mark.parametrize("fp4,n,k,silu", [(True, 256, 512, False), (True, 4096, 4096, False), (True, 144, 320, False),
+                                          (True, 512, 256, True), (False, 256, 512, False), (False, 96, 144, True)])
+def test_gemv_past_64_tokens(m, fp4, n, k, silu):
+    """65..192 tokens: one launch per 64 tokens (the last one ragged), NVFP4
+    and BF16 weights, silu_mul."""
+    _say("gemv past 64 tokens", m, fp4, n, k, silu)
+    if fp4:
+        d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 5 * n + k)
+        got = run_nvfp4(d, n, silu=silu)
+        want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=silu)
+        gs = d["gs"][0]
+    else:
+        d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 5 * n + k)
+        got = run_bf16(d, silu=silu)
+        want, acc, absacc = oracle.bf16_gemv(d["x"], d["w"], silu_mul=silu)
+        gs = 1.0
+    if silu:
+        check_silu(got, want, acc, absacc, gs, f"{m} tokens silu N={n} K={k}")
+    else:
+        check_gemv(got, acc, absacc, gs, k, f"{m} tokens N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [100, 192])
+def test_gemv_splitk_past_64_tokens(m):
+    """The split-K entry point past 64 tokens: every 64-token launch reuses
+    the workspace (its counters are zero again after each), strided x."""
+    n, k = 1024, 8192
+    d = synth.dense_w4a16(m, n, k, seed=1300 + m)
+    wide = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    wide[:, :k] = d["x"]
+    xv = dev(wide)[:, :k]
+    _say("splitk past 64", m, lib.gemv_kernel_name(m, n, k, splitk=True))
+    ws = lib.gemv_splitk_workspace(m, n, k, device=DEV)
+    out = lib.nvfp4_gemv_splitk(xv, dev(d["w"]), dev(d["s"]), dev(d["gs"]), workspace=ws)
+    torch.cuda.synchronize()
+    _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
+    check_gemv(to_bits(out.cpu()), acc, absacc, d["gs"][0], k, f"splitk {m} tokens")
+    assert int(ws[:65536].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("m", [40, 64])
 @pytest.mark.parametrize("n,k,silu", [(256, 512, False), (96, 144, False), (512, 256, True)])
 def test_bf16_gemv_up_to_64_tokens(m, n, k, silu):
@@ -447,7 +488,7 @@ def test_nvfp4_gemv_is_deterministic(m):
 
 
 def test_nvfp4_gemv_rejects_bad_shapes():
-    d = synth.dense_w4a16(65, 256, 512, seed=1)  # one token past the limit
+    d = synth.dense_w4a16(193, 256, 512, seed=1)  # one token past the limit
     with pytest.raises(lib.W4A16Error):
         lib.nvfp4_gemv(dev(d["x"]), dev(d["w"]), dev(d["s"]), dev(d["gs"]))
 

@@ -91,7 +91,8 @@ int run_gemv(bool fp4, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
   p.K = static_cast<int>(K);
   p.half = silu_mul ? static_cast<int>(N / 2) : 0;
   if (splitk) {
-    const w4a16::SplitPlan plan = w4a16::gemv_split_plan(fp4, M, N, K, silu_mul);
+    const int64_t m_launch = M < W4A16_GEMV_TOKENS_PER_LAUNCH ? M : W4A16_GEMV_TOKENS_PER_LAUNCH;
+    const w4a16::SplitPlan plan = w4a16::gemv_split_plan(fp4, m_launch, N, K, silu_mul);
     if (plan.s > 1) {
       if (!workspace) return fail(W4A16_ERR_INVALID_ARG, "null workspace (%lld bytes needed)", plan.bytes);
       if (workspace_bytes < plan.bytes)
@@ -106,8 +107,22 @@ int run_gemv(bool fp4, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
   // The VALU kernels read a quad's scale words as one 16-byte chunk; a scale
   // buffer that is only 4-byte aligned goes to the MFMA kernels, which read
   // one 4-byte word per row.
-  const int path = (!fp4 || aligned(w_scale, 16)) ? w4a16::choose_gemv_path(fp4, M, N, K) : w4a16::kPathMfma;
-  return hip_status(w4a16::launch_gemv(fp4, p, silu_mul, path, static_cast<hipStream_t>(stream)));
+  const bool s16 = !fp4 || aligned(w_scale, 16);
+  // Beyond 64 tokens, one launch per 64 tokens (stream-ordered, so the
+  // split-K form's counters are free again for the next launch).
+  const int64_t n_out = silu_mul ? N / 2 : N;
+  for (int64_t m0 = 0; m0 < M; m0 += W4A16_GEMV_TOKENS_PER_LAUNCH) {
+    const int64_t mc = M - m0 < W4A16_GEMV_TOKENS_PER_LAUNCH ? M - m0 : W4A16_GEMV_TOKENS_PER_LAUNCH;
+    w4a16::GemvParams q = p;
+    q.x = x + m0 * ldx;
+    q.x_bytes = static_cast<uint32_t>(((mc - 1) * ldx + K) * 2);
+    q.out = out + m0 * n_out;
+    q.M = static_cast<int>(mc);
+    const int path = s16 ? w4a16::choose_gemv_path(fp4, mc, N, K) : w4a16::kPathMfma;
+    const int st2 = hip_status(w4a16::launch_gemv(fp4, q, silu_mul, path, static_cast<hipStream_t>(stream)));
+    if (st2 != W4A16_OK) return st2;
+  }
+  return W4A16_OK;
 }
 
 const char* gemv_kernel_name_of(int weight_fp4, int64_t M, int64_t N, int64_t K, int silu_mul, bool splitk) {
@@ -126,19 +141,21 @@ const char* gemv_kernel_name_of(int weight_fp4, int64_t M, int64_t N, int64_t K,
     fail(W4A16_ERR_INVALID_ARG, "M=0 launches no kernel");
     return name;
   }
+  // the kernel of the first launch (calls past 64 tokens launch once per 64)
+  const int64_t m_launch = M < W4A16_GEMV_TOKENS_PER_LAUNCH ? M : W4A16_GEMV_TOKENS_PER_LAUNCH;
   w4a16::GemvParams p{};
   p.ldx = K;
-  p.M = static_cast<int>(M);
+  p.M = static_cast<int>(m_launch);
   p.N = static_cast<int>(N);
   p.K = static_cast<int>(K);
   p.half = silu_mul ? static_cast<int>(N / 2) : 0;
   const bool fp4 = weight_fp4 != 0;
-  if (splitk && w4a16::gemv_split_plan(fp4, M, N, K, silu_mul).s > 1) {
+  if (splitk && w4a16::gemv_split_plan(fp4, m_launch, N, K, silu_mul).s > 1) {
     // a stand-in workspace: the dispatch only checks that there is one
     p.part = reinterpret_cast<float*>(uintptr_t(256));
     p.cnt = reinterpret_cast<uint32_t*>(uintptr_t(256));
   }
-  w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, M, N, K), name, sizeof name);
+  w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, m_launch, N, K), name, sizeof name);
   ok();
   return name;
 }
@@ -181,7 +198,8 @@ int64_t gemv_splitk_workspace_bytes(int weight_fp4, int64_t M, int64_t N, int64_
                   weight_fp4 ? 64 : 16) != W4A16_OK)
     return -1;
   ok();
-  return M == 0 ? 0 : w4a16::gemv_split_plan(weight_fp4 != 0, M, N, K, silu_mul).bytes;
+  const int64_t m_launch = M < W4A16_GEMV_TOKENS_PER_LAUNCH ? M : W4A16_GEMV_TOKENS_PER_LAUNCH;
+  return M == 0 ? 0 : w4a16::gemv_split_plan(weight_fp4 != 0, m_launch, N, K, silu_mul).bytes;
 }
 
 int nvfp4_gemv_splitk(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint8_t* w,
@@ -199,7 +217,8 @@ int nvfp4_gemv_splitk_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t l
   const uint16_t* stand_in = reinterpret_cast<const uint16_t*>(uintptr_t(256));
   int st = check_dense(stand_in, M, K, K, stand_in, N, silu_mul, reinterpret_cast<uint16_t*>(uintptr_t(256)), 64);
   if (st != W4A16_OK || M == 0) return st;
-  const int64_t need = w4a16::gemv_split_plan(true, M, N, K, silu_mul).bytes;
+  const int64_t m_launch = M < W4A16_GEMV_TOKENS_PER_LAUNCH ? M : W4A16_GEMV_TOKENS_PER_LAUNCH;
+  const int64_t need = w4a16::gemv_split_plan(true, m_launch, N, K, silu_mul).bytes;
   if (need > W4A16_NOALLOC_SCRATCH_BYTES)
     return fail(W4A16_ERR_UNSUPPORTED, "the split-K plan needs %lld bytes of scratch, the library holds %lld", need,
                 W4A16_NOALLOC_SCRATCH_BYTES);
