@@ -4,10 +4,13 @@
  * C ABI of libw4a16_nvfp4_gemv.so.  Every entry point takes plain device
  * pointers and sizes, enqueues its kernels asynchronously on `stream` (a
  * hipStream_t; NULL means the legacy default stream) and returns a status
- * code.  The library never allocates device memory, never synchronizes the
- * stream and never aborts: a call that cannot run returns a non-zero status
- * and enqueues nothing.  All buffers are owned by the caller and must stay
- * alive until the enqueued work has finished.
+ * code.  No entry point synchronizes the stream or aborts: a call that
+ * cannot run returns a non-zero status and enqueues nothing.  No entry point
+ * allocates device memory, with one exception: the first nvfp4_dequant_gemm
+ * call on a device creates that device's rocBLAS handle, which holds
+ * rocBLAS's own device memory until the process ends (make that first call
+ * outside HIP graph capture).  All buffers are owned by the caller and must
+ * stay alive until the enqueued work has finished.
  *
  * Data formats (the "ModelOpt layout" of the pages vllm.models.flint.ops.
  * nvfp4_gemv, module docstring, and vllm.models.flint.ops.linear,

@@ -1,6 +1,8 @@
 // C ABI of the library: argument validation, path choice and launch.
-// No entry point allocates memory, synchronizes or aborts; a call that
-// cannot run returns a non-zero status and enqueues nothing.
+// No entry point synchronizes or aborts; a call that cannot run returns a
+// non-zero status and enqueues nothing.  None allocates device memory except
+// nvfp4_dequant_gemm, whose first call on a device creates that device's
+// rocBLAS handle (rocBLAS's own device memory, kept until the process ends).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
