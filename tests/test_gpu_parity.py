@@ -597,6 +597,42 @@ def test_moe_small_shapes(m, e, topk, h, inter, si):
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe M={m}")
 
 
+@pytest.mark.parametrize("m,ids", [
+    (1, [[3, 3, 1, 3]]),
+    (2, [[0, 5, 0, 2], [5, 5, 5, 5]]),
+])
+def test_moe_duplicate_experts_one_or_two_tokens(m, ids):
+    """One or two tokens (the forms with one job per pair): pairs routed to
+    the same expert, within a token and across the two tokens."""
+    e, topk, h, inter, si = 6, 4, 256, 192, 128
+    wts = synth.moe_weights(e, h, inter, si, seed=353 + m)
+    tok = synth.moe_tokens(m, h, e, topk, seed=354 + m)
+    tok["ids"] = torch.tensor(ids, dtype=torch.int32)
+    _say("moe duplicates", m, e, topk)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), f"moe duplicates M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("h,inter,si", [
+    (128, 512, 64),       # down_combine: one wave
+    (192, 1024, 512),     # two waves
+    (2048, 1536, 1536),   # three waves, one chunk per lane; gate_up one chunk per lane
+    (128, 4096, 256),     # four waves, two chunks per lane
+    (4160, 1024, 1024),   # gate_up: two chunks per lane, two K blocks
+    (128, 4160, 64),      # I beyond the one-block down_combine: the MFMA form
+])
+def test_moe_one_or_two_tokens_k_extents(m, h, inter, si):
+    """The K extents that select the waves and chunks of the one-job-per-pair
+    forms (and the fallback past them), top-8 of 16 experts."""
+    e, topk = 16, 8
+    wts = synth.moe_weights(e, h, inter, si, seed=380 + m + inter)
+    tok = synth.moe_tokens(m, h, e, topk, seed=390 + m + inter)
+    _say("moe K extents", m, h, inter, si)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), f"moe K extents M={m} H={h} I={inter} SI={si}")
+
+
 def test_moe_duplicate_experts_within_a_token():
     """A token routed twice to one expert: both slots count (two act rows,
     two weighted terms of the combine)."""

@@ -1,12 +1,5 @@
 // Expert-indexed MoE decode pair (moe_gemv page, module docstring and the
-// gate_up / down_combine docstrings), expert-major: every routed expert's
-// weights are read once per call, for all the tokens routed to it.
-//
-// Routing.  Every workgroup rebuilds the call's routing in LDS from ids (at
-// most 32 tokens x 16 slots = 512 pairs): the distinct experts in order of
-// first appearance ("slots"), and the pairs of every slot in ascending pair
-// order.  No host synchronization and no workspace are needed, and the order
-// of every floating-point sum depends on ids alone.
+// gate_up / down_combine docstrings).
 //
 //   gate_up routed: act[p][i] = bf16(silu(g) * u),  g, u = FP32 sum * alpha[e]
 //   gate_up shared: sact[t][i] = bf16(silu(bf16(g)) * bf16(u)),  g, u = FP32 sum * gssh
@@ -15,15 +8,23 @@
 //
 // Two forms of each kernel:
 //
-// VALU forms (M <= 2).  Chunk-interleaved loads and per-token dot products
-// (chunk_core.hpp).  gate_up walks persistent items (slot, quad of gate rows
-// and the matching up rows) with four waves splitting H and meeting in LDS;
-// down_combine gives a workgroup a quad of H rows, its waves take the slots
-// round robin and stream their jobs (slot, token group, K block) through a
-// two-slot ring of registers.
+// VALU forms (M <= 2).  One job per pair: a job reads the weights of its
+// pair's expert (two pairs routed to one expert read them twice, the second
+// time mostly from L2), so no routing table is built and a workgroup needs
+// only the ids of its jobs.  Chunk-interleaved loads and per-token dot
+// products (chunk_core.hpp).  gate_up gives every (shared expert or pair,
+// quad of gate rows and the matching up rows) item a workgroup whose four
+// waves split H; down_combine gives a workgroup a quad of H rows and puts
+// the loads of up to 9 jobs in flight at once.
 //
-// MFMA forms (M >= 3).  The swap-AB MFMA building blocks of the dense GEMV
-// (mfma_core.hpp) with each slot's tokens gathered by the loads that stage
+// MFMA forms (M >= 3), expert-major: every routed expert's weights are read
+// once per call, for all the tokens routed to it.  Every workgroup rebuilds
+// the call's routing in LDS from ids (at most 32 tokens x 16 slots = 512
+// pairs): the distinct experts in order of first appearance ("slots"), and
+// the pairs of every slot in ascending pair order.  No host synchronization
+// and no workspace are needed, and the order of every floating-point sum
+// depends on ids alone.  The swap-AB MFMA building blocks of the dense GEMV
+// (mfma_core.hpp) take each slot's tokens, gathered by the loads that stage
 // activations in LDS; the dequant then costs the same for any number of
 // tokens.  Each wave streams whole work units through one LDS ring (see the
 // section below).
@@ -31,6 +32,8 @@
 // Inside every ring the loads are counted: no other vector memory access may
 // fall between them, and LDS tables are read with lds_read_u32 so that the
 // compiler adds no wait for the loads still writing ring slots.
+#include <type_traits>
+
 #include "chunk_core.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -90,18 +93,8 @@ struct alignas(16) MoeRouting {
   int32_t D;                        // distinct experts
 };
 
-// The routing the VALU forms need for their at most 2 x 16 pairs (the fields
-// of MoeRouting they read), about 0.7 KB of LDS instead of 26 KB, so that
-// LDS does not bound how many of their workgroups a compute unit holds.
+// Pairs the VALU forms (one or two tokens) take: at most 2 x 16.
 constexpr int kMoeValuMaxPairs = 32;
-struct alignas(16) MoeRoutingSmall {
-  int32_t expert[kMoeValuMaxPairs];
-  int32_t count[kMoeValuMaxPairs];
-  int32_t start[kMoeValuMaxPairs + 1];
-  int32_t order[kMoeValuMaxPairs];
-  float tw[kMoeValuMaxPairs];
-  int32_t D;
-};
 
 // Number of i in [lo, hi) with a[i] == v: a scan of an LDS array in blocks of
 // 16 entries read as four 16-byte broadcasts (the array is readable up to
@@ -207,86 +200,27 @@ __device__ void build_routing(MoeRouting& r, const int32_t* ids, const float* tw
   __syncthreads();
 }
 
-// The same routing for at most 64 pairs (one per lane of the first wave),
-// with cross-lane reads instead of LDS tables: the other waves only wait at
-// the closing barrier.  The VALU forms (one or two tokens: at most 32 pairs)
-// use it; a decode step's few pairs then cost a handful of scalar loops
-// instead of the table passes and their barriers (measured 0.5 / 0.8 us off
-// gate_up / down_combine at one token).  The MFMA forms keep the table
-// builder: with both builders in them they ran 12-16% slower at 8 and 32
-// tokens.
-template <typename Routing>
-__device__ void build_routing_wave(Routing& r, const int32_t* ids, const float* tw, int P, int E) {
-  if (threadIdx.x < 64) {
-    const int p = threadIdx.x;
-    const bool live = p < P;
-    // absent pairs get distinct negative ids, so they match nothing
-    const int e = live ? clamp_expert(ids[p], E) : -1 - p;
-    int first = p, within = 0;
-    for (int q = 0; q < P; ++q) {
-      const int eq = __builtin_amdgcn_readlane(e, q);
-      if (q < p && eq == e) {
-        ++within;
-        first = q < first ? q : first;
-      }
-    }
-    const bool is_first = live && first == p;
-    const uint64_t firsts = __ballot(is_first);
-    const int slot_if_first = __popcll(firsts & ((uint64_t(1) << p) - 1));
-    int count = 0;
-    for (int q = 0; q < P; ++q) count += __builtin_amdgcn_readlane(first, q) == p ? 1 : 0;
-    // start of a first pair's slot: the counts of the first pairs before it
-    int start = 0;
-    for (int q = 0; q < P; ++q) {  // a uniform loop: q is the same on every lane
-      const int fq = __builtin_amdgcn_readlane(first, q);
-      const int cq = __builtin_amdgcn_readlane(count, q);
-      start += (q < p && fq == q) ? cq : 0;
-    }
-    const int my_start = __shfl(start, first);
-    if (is_first) {
-      r.expert[slot_if_first] = e;
-      r.count[slot_if_first] = count;
-      r.start[slot_if_first] = start;
-    }
-    if (live) {
-      r.order[my_start + within] = p;
-      if (tw) r.tw[p] = tw[p];
-    }
-    if (p == 0) {
-      r.D = __popcll(firsts);
-      r.start[__popcll(firsts)] = P;
-    }
-  }
-  __syncthreads();
-}
-
-
-// ------------------------------------------------------------------ gate_up
-// Work items are (slot, gate quad of the expert's I rows) and (gate quad of
-// the shared expert's SI rows); a persistent grid builds the routing once per
-// workgroup and walks the items.  For an item, the four waves split H; the
-// expert's gate and up quads are read once (per K block) and applied to the
-// slot's tokens MT at a time.  Each item is straight-line: all of its loads
-// are issued before its arithmetic, and its results are stored before the
-// next item's loads (so no wait ever mixes stores and loads in flight).
+// ------------------------------------------------------------------ gate_up, one job per pair
+// One or two tokens: items are (shared expert, quad of SI rows) -- first,
+// since they need no id -- and (pair j, quad of I rows) for every pair, so
+// a workgroup needs only the id of its item's pair, read by one scalar-
+// uniform load, and no routing table.  Two pairs routed to one expert read
+// its weights twice (the second time mostly from L2).  An item reads its
+// gate and up quads once and applies them to its tokens (the pair's token,
+// or all M tokens for the shared expert) with the chunked VALU core; the 4
+// waves split H.
 template <int MT, int C>
-__global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
+__global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams p) {
   constexpr int KS = 4;                 // waves per item, each a slice of H
   constexpr int PV = 2;                 // gate, up
-  constexpr int V = MT * 4 * PV;        // value index (m * 4 + q) * 2 + u
-  using RS = ReduceScatter<V, PV>;
-  __shared__ MoeRoutingSmall rt;
-  __shared__ float red[KS - 1][RS::LEFT][64];
+  __shared__ float red[KS - 1][MT * 4 * PV][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kw = uniform(tid >> 6);
-  const int P = p.M * p.topk;  // at most 2 x 16: one wave builds the routing
-  build_routing_wave(rt, p.ids, nullptr, P, p.E);
-  const int D = uniform(rt.D);
-  // 32-bit item bookkeeping: at most 512 slots x (I / 4) quads
+  const int P = p.M * p.topk;
   const int units_r = (p.I + 127) / 128 * 32;
   const int units_s = (p.SI + 127) / 128 * 32;
-  const int items = D * units_r + units_s;
+  const int items = P * units_r + units_s;
   const uint32_t nch = p.H / 8;
   const int nkb = static_cast<int>((nch + KS * C * 64 - 1) / (KS * C * 64));
   const uint32_t shift = 8u * ((lane >> 1) & 3);
@@ -295,15 +229,11 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
   const rsrc_t rx = make_rsrc(p.x, static_cast<uint32_t>(p.M) * p.H * 2);
   const float gssh = *p.gssh;
 
-  for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
-    const bool shared = item >= D * units_r;
-    const int s = shared ? 0 : item / units_r;
-    const int u = shared ? item - D * units_r : item - s * units_r;
-    const int e = shared ? 0 : uniform(rt.expert[s]);
-    const int cnt = shared ? p.M : uniform(rt.count[s]);
-    const int first = shared ? 0 : uniform(rt.start[s]);
+  auto run = [&](auto nt_tag, bool shared, int j, int u, int e, float scale) {
+    constexpr int NT = decltype(nt_tag)::value;  // token rows of the item
+    constexpr int V = NT * 4 * PV;               // value index (m * 4 + q) * 2 + w
+    using RS = ReduceScatter<V, PV>;
     const int half = shared ? p.SI : p.I;
-    const float scale = shared ? gssh : p.alpha[e];
     int64_t rows[8];
     bool rv[8];
     quad_rows<8>(u, half, half, rows, rv);
@@ -312,238 +242,201 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const MoeGateUpParams p) {
                                    static_cast<uint32_t>(shared ? p.wsh_bytes : p.w1_expert_bytes));
     const rsrc_t rs = uniform_rsrc(shared ? p.ssh : p.w1s + e * p.s1_expert_bytes,
                                    static_cast<uint32_t>(shared ? p.ssh_bytes : p.s1_expert_bytes));
-
-    for (int g0 = 0; g0 < cnt; g0 += MT) {
-      // token rows of this group (pairs of the slot in ascending order)
-      uint32_t xoff[MT];
+    uint32_t xoff[NT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int idx = g0 + m;
-        const int t = shared ? idx : rt.order[first + (idx < cnt ? idx : cnt - 1)] / p.topk;
-        xoff[m] = off_if(idx < cnt, static_cast<uint32_t>(t) * p.H * 2);
+    for (int m = 0; m < NT; ++m) {
+      const int t = shared ? m : j / p.topk;
+      xoff[m] = off_if(shared ? m < p.M : true, static_cast<uint32_t>(t) * p.H * 2);
+    }
+    float acc[8][NT];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int m = 0; m < NT; ++m) acc[i][m] = 0.0f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      uint32_t ch[C];
+      bool ok[C];
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        ch[q] = static_cast<uint32_t>((kb * KS + kw) * C + q) * 64 + lane;
+        ok[q] = ch[q] < nch;
       }
-      float acc[8][MT];
+      ChunkX<C, NT> xb;
+      ChunkW<C, 8> wb;
+      chunk_issue_x<C, NT>(xb, rx, xoff, ch, ok);
+      chunk_issue_w<C, 8>(wb, rw, row_bytes, rs, tiles, rows, rv, quad_ok, ch, ok);
+      __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
+      chunk_compute<C, 8, NT>(wb, xb, shift, acc);
+    }
+    float v[V];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int m = 0; m < NT; ++m)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
-      for (int kb = 0; kb < nkb; ++kb) {
-        uint32_t ch[C];
-        bool ok[C];
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int q = 0; q < C; ++q) {
-          ch[q] = static_cast<uint32_t>((kb * KS + kw) * C + q) * 64 + lane;
-          ok[q] = ch[q] < nch;
-        }
-        ChunkX<C, MT> xb;
-        ChunkW<C, 8> wb;
-        chunk_issue_x<C, MT>(xb, rx, xoff, ch, ok);
-        chunk_issue_w<C, 8>(wb, rw, row_bytes, rs, tiles, rows, rv, quad_ok, ch, ok);
-        __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
-        chunk_compute<C, 8, MT>(wb, xb, shift, acc);
-      }
-      float v[V];
+        for (int w = 0; w < PV; ++w) v[(m * 4 + q) * PV + w] = acc[4 * w + q][m];
+    reduce_scatter<V, PV>(v);
+    if (kw > 0) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int i = 0; i < RS::LEFT; ++i) red[kw - 1][i][lane] = v[i];
+    }
+    __syncthreads();
+    if (kw == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+      for (int w = 0; w < KS - 1; ++w)
 #pragma unroll
-          for (int w = 0; w < PV; ++w) v[(m * 4 + q) * PV + w] = acc[4 * w + q][m];
-      reduce_scatter<V, PV>(v);
-      if (kw > 0) {
+        for (int i = 0; i < RS::LEFT; ++i) v[i] += red[w][i][lane];
+      const int base = reduce_scatter_base<V, PV>(lane);
 #pragma unroll
-        for (int i = 0; i < RS::LEFT; ++i) red[kw - 1][i][lane] = v[i];
-      }
-      __syncthreads();
-      if (kw == 0) {
-#pragma unroll
-        for (int w = 0; w < KS - 1; ++w)
-#pragma unroll
-          for (int i = 0; i < RS::LEFT; ++i) v[i] += red[w][i][lane];
-        const int base = reduce_scatter_base<V, PV>(lane);
-#pragma unroll
-        for (int i = 0; i < RS::LEFT / PV; ++i) {
-          const int vi = base + i * PV;
-          const int m = vi / (4 * PV), q = (vi / PV) % 4;
-          const int idx = g0 + m;
-          const int64_t row = static_cast<int64_t>(u >> 5) * 128 + (u & 31) + 32 * q;
-          if ((lane & 15) == i && idx < cnt && row < half) {
-            float g = v[i * PV] * scale, up = v[i * PV + 1] * scale;
-            if (shared) {
-              g = bf16_bits_to_f32(f32_to_bf16_bits(g));
-              up = bf16_bits_to_f32(f32_to_bf16_bits(up));
-              p.sact[static_cast<int64_t>(idx) * p.SI + row] = f32_to_bf16_bits(silu_f32(g) * up);
-            } else {
-              const int pair = rt.order[first + idx];
-              p.act[static_cast<int64_t>(pair) * p.I + row] = f32_to_bf16_bits(silu_f32(g) * up);
-            }
+      for (int i = 0; i < RS::LEFT / PV; ++i) {
+        const int vi = base + i * PV;
+        const int m = vi / (4 * PV), q = (vi / PV) % 4;
+        const int64_t row = static_cast<int64_t>(u >> 5) * 128 + (u & 31) + 32 * q;
+        if ((lane & 15) == i && row < half && (!shared || m < p.M)) {
+          float g = v[i * PV] * scale, up = v[i * PV + 1] * scale;
+          if (shared) {
+            g = bf16_bits_to_f32(f32_to_bf16_bits(g));
+            up = bf16_bits_to_f32(f32_to_bf16_bits(up));
+            p.sact[static_cast<int64_t>(m) * p.SI + row] = f32_to_bf16_bits(silu_f32(g) * up);
+          } else {
+            p.act[static_cast<int64_t>(j) * p.I + row] = f32_to_bf16_bits(silu_f32(g) * up);
           }
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+  };
+
+  for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
+    if (item < units_s) {
+      run(std::integral_constant<int, MT>{}, true, 0, item, 0, gssh);
+    } else {
+      const int j = (item - units_s) / units_r;
+      const int u = item - units_s - j * units_r;
+      const int e = clamp_expert(uniform(p.ids[j]), p.E);
+      run(std::integral_constant<int, 1>{}, false, j, u, e, p.alpha[e]);
     }
   }
 }
 
-// ------------------------------------------------------------------ down_combine
-template <int MT, int C, int NW>
-__global__ __launch_bounds__(NW * 64) void k_moe_down_combine(const MoeDownParams p) {
-  constexpr int V = MT * 4;  // value index m * 4 + q
+// ------------------------------------------------------------------ down_combine, one job per pair
+// One or two tokens: the work of a quad of H rows is P + M jobs, the shared
+// expert for each token and then every pair in order (pair j reads the
+// weights of expert ids[j] and its own act row; two pairs routed to one
+// expert read its weights twice, the second time from L2).  No routing table
+// is built: a job needs only its pair's id, and the shared jobs, which need
+// none, are issued while the ids arrive.  The NW waves split the K of every
+// job (lane l of wave w takes chunks (c * NW + w) * 64 + l), so all SG jobs
+// of a group are in flight at once; their sums are reduced across the lanes
+// and waves, rounded to BF16 (y_j = bf16(acc * alpha2[e_j]), y_shared =
+// bf16(acc * gssd)), and the combine adds tw_j * y_j over j in ascending
+// order in FP32 before the two BF16 roundings of the moe_gemv page.
+constexpr int kMoeDownPairsMaxJobs = kMoeValuMaxPairs + 2;
+
+template <int NW, int CL, int SG>
+__global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams p) {
+  constexpr int R = 4;       // rows of a workgroup: one quad of H rows
+  constexpr int V = SG * R;  // value index job * R + q
   using RS = ReduceScatter<V, 1>;
-  __shared__ MoeRoutingSmall rt;
-  __shared__ float part[NW][kMoeMaxTokens][4];
-  __shared__ float ysh[kMoeMaxTokens][4];
+  __shared__ float red[NW][V];
+  __shared__ float yv[kMoeDownPairsMaxJobs][R];  // jobs 0..M-1: shared expert, then pairs
+  __shared__ float tws[kMoeValuMaxPairs];
+  __shared__ float a2s[kMoeValuMaxPairs];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int P = p.M * p.topk;  // at most 2 x 16: one wave builds the routing
-  build_routing_wave(rt, p.ids, p.tw, P, p.E);
-  const int D = uniform(rt.D);
+  const int P = p.M * p.topk;
+  const int J = p.M + P;
+  // every pair's id, alpha2 and routing weight, issued first (vector loads:
+  // the waits the compiler adds for them come after the shared jobs' loads)
+  const int my_e = lane < P ? clamp_expert(p.ids[lane], p.E) : 0;
+  const float my_tw = lane < P ? p.tw[lane] : 0.0f;
+  const float my_a2 = lane < P ? p.alpha2[my_e] : 0.0f;
   const float gssd = *p.gssd;
   const int64_t units = (p.H + 127) / 128 * 32;
   const uint32_t shift = 8u * ((lane >> 1) & 3);
   const uint32_t act_bytes = static_cast<uint32_t>(P) * p.I * 2;
   const uint32_t sact_bytes = static_cast<uint32_t>(p.M) * p.SI * 2;
-
-  // Job = (slot s, group of MT tokens from g0, K block kb); wave w takes the
-  // slots s = w, w + NW, ...; slot D is the shared expert.
-  struct Job {
-    int s, g0, kb;
-  };
-  auto npairs_of = [&](int s) -> int {
-    const int cnt = uniform(rt.count[s < D ? s : D - 1]);
-    return s < D ? cnt : p.M;
-  };
-  auto nkb_of = [&](int s) -> int {
-    const int k = s < D ? p.I : p.SI;
-    return (k / 8 + C * 64 - 1) / (C * 64);
-  };
-  auto advance = [&](Job j) -> Job {
-    if (++j.kb == nkb_of(j.s)) {
-      j.kb = 0;
-      j.g0 += MT;
-      if (j.g0 >= npairs_of(j.s)) {
-        j.g0 = 0;
-        j.s += NW;
-      }
-    }
-    return j;
-  };
-  int njobs = 0;
-  for (int s = wave; s <= D; s += NW) njobs += (npairs_of(s) + MT - 1) / MT * nkb_of(s);
+  bool tw_stored = false;
 
   for (int64_t u = xcd_logical_block(); u < units; u += gridDim.x) {
-    int64_t rows[4];
-    bool rv[4];
-    quad_rows<4>(u, p.H, 0, rows, rv);
-    for (int i = lane; i < p.M * 4; i += 64) part[wave][i >> 2][i & 3] = 0.0f;
-
-    auto issue = [&](const Job& j, ChunkW<C, 4>& wb, ChunkX<C, MT>& xb) {
-      const bool valid = j.s <= D;
-      const bool shared = j.s == D;
-      const int e = uniform(rt.expert[j.s < D ? j.s : D - 1]);
-      const int k = shared ? p.SI : p.I;
-      const uint32_t nch = k / 8;
-      uint32_t ch[C];
-      bool ok[C];
+    int64_t rows[R];
+    bool rv[R];
+    quad_rows<R>(u, p.H, 0, rows, rv);
+    const bool quad_ok[1] = {true};
+    for (int g0 = 0; g0 < J; g0 += SG) {
+      ChunkW<CL, R> wb[SG];
+      ChunkX<CL, 1> xb[SG];
 #pragma unroll
-      for (int q = 0; q < C; ++q) {
-        ch[q] = static_cast<uint32_t>(j.kb * C + q) * 64 + lane;
-        ok[q] = valid && ch[q] < nch;
-      }
-      const int np = valid ? npairs_of(j.s) : 0;
-      const int first = rt.start[j.s < D ? j.s : D];
-      uint32_t xoff[MT];
+      for (int s = 0; s < SG; ++s) {
+        const int j = g0 + s;
+        const bool valid = j < J;
+        const bool shared = j < p.M;
+        const int pair = shared ? 0 : (valid ? j - p.M : 0);
+        const int e = shared ? 0 : __builtin_amdgcn_readlane(my_e, pair);
+        const int k = shared ? p.SI : p.I;
+        const uint32_t nch = k / 8;
+        uint32_t ch[CL];
+        bool ok[CL];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int idx = j.g0 + m;
-        const int o = first + idx;
-        const int row = shared ? idx : rt.order[o < P ? o : P - 1];
-        xoff[m] = off_if(idx < np, static_cast<uint32_t>(row) * k * 2);
+        for (int c = 0; c < CL; ++c) {
+          ch[c] = static_cast<uint32_t>(c * NW + wave) * 64 + lane;
+          ok[c] = valid && ch[c] < nch;
+        }
+        const uint32_t xoff[1] = {static_cast<uint32_t>(shared ? j : pair) * k * 2};
+        chunk_issue_x<CL, 1>(xb[s],
+                             uniform_rsrc(shared ? static_cast<const void*>(p.sact) : static_cast<const void*>(p.act),
+                                          shared ? sact_bytes : act_bytes),
+                             xoff, ch, ok);
+        const uint8_t* wbase = shared ? p.wsd : p.w2 + e * p.w2_expert_bytes;
+        const uint8_t* sbase = shared ? p.ssd : p.w2s + e * p.s2_expert_bytes;
+        const uint32_t wbytes = static_cast<uint32_t>(shared ? p.wsd_bytes : p.w2_expert_bytes);
+        const uint32_t sbytes = static_cast<uint32_t>(shared ? p.ssd_bytes : p.s2_expert_bytes);
+        chunk_issue_w<CL, R>(wb[s], uniform_rsrc(wbase, wbytes), k / 2, uniform_rsrc(sbase, sbytes), k / 64, rows, rv,
+                             quad_ok, ch, ok);
       }
-      chunk_issue_x<C, MT>(xb, uniform_rsrc(shared ? static_cast<const void*>(p.sact) : static_cast<const void*>(p.act),
-                                            shared ? sact_bytes : act_bytes),
-                           xoff, ch, ok);
-      const bool quad_ok[1] = {true};
-      const uint8_t* wbase = shared ? p.wsd : p.w2 + e * p.w2_expert_bytes;
-      const uint8_t* sbase = shared ? p.ssd : p.w2s + e * p.s2_expert_bytes;
-      const uint32_t wbytes = static_cast<uint32_t>(shared ? p.wsd_bytes : p.w2_expert_bytes);
-      const uint32_t sbytes = static_cast<uint32_t>(shared ? p.ssd_bytes : p.s2_expert_bytes);
-      chunk_issue_w<C, 4>(wb, uniform_rsrc(wbase, wbytes), k / 2, uniform_rsrc(sbase, sbytes), k / 64, rows, rv,
-                          quad_ok, ch, ok);
-      __builtin_amdgcn_sched_barrier(0);  // as in k_moe_gate_up
-    };
-
-    float acc[4][MT];
-    auto finish = [&](const Job& j) {
-      const bool shared = j.s == D;
-      // a scalar load: it does not count against the vector loads in flight
-      const float scale = shared ? gssd : p.alpha2[uniform(rt.expert[j.s < D ? j.s : D - 1])];
-      const int np = npairs_of(j.s);
-      const int first = rt.start[j.s < D ? j.s : D];
+      __builtin_amdgcn_sched_barrier(0);  // every load of the group ahead of the arithmetic
       float v[V];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int s = 0; s < SG; ++s) {
+        float acc[R][1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[m * 4 + q] = acc[q][m];
+        for (int i = 0; i < R; ++i) acc[i][0] = 0.0f;
+        chunk_compute<CL, R, 1>(wb[s], xb[s], shift, acc);
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[s * R + i] = acc[i][0];
+      }
       reduce_scatter<V, 1>(v);
       const int base = reduce_scatter_base<V, 1>(lane);
-      // one token at a time: two pairs of one token routed to the same
-      // expert must not update its partial in the same instruction
+      if ((lane & 15) == 0) {
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) {
+        for (int i = 0; i < RS::LEFT; ++i) red[wave][base + i] = v[i];
+      }
+      if (!tw_stored && wave == 0 && lane < P) {
+        tws[lane] = my_tw;
+        a2s[lane] = my_a2;
+      }
+      tw_stored = true;
+      __syncthreads();
+      if (tid < V) {
+        const int j = g0 + tid / R;
+        if (j < J) {
+          float t = red[0][tid];
 #pragma unroll
-        for (int i = 0; i < RS::LEFT; ++i) {
-          const int vi = base + i;
-          const int m = vi / 4, q = vi % 4;
-          const int idx = j.g0 + m;
-          if (m == mm && (lane & 15) == i && idx < np) {
-            const float y = bf16_bits_to_f32(f32_to_bf16_bits(v[i] * scale));
-            if (shared) {
-              ysh[idx][q] = y;
-            } else {
-              const int pair = rt.order[first + idx];
-              part[wave][pair / p.topk][q] += rt.tw[pair] * y;
-            }
-          }
+          for (int w = 1; w < NW; ++w) t += red[w][tid];  // in wave order
+          const float scale = j < p.M ? gssd : a2s[j - p.M];
+          yv[j][tid % R] = bf16_bits_to_f32(f32_to_bf16_bits(t * scale));
         }
       }
-    };
-
-    ChunkW<C, 4> wa, wb;
-    ChunkX<C, MT> xa, xb;
-    Job ja{wave, 0, 0};
-    Job jb = advance(ja);
-    issue(ja, wa, xa);
-    issue(jb, wb, xb);  // jobs past the last slot read nothing
-    auto consume = [&](const Job& j, const ChunkW<C, 4>& w, const ChunkX<C, MT>& x) {
-      if (j.kb == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acc[i][m] = 0.0f;
-      }
-      chunk_compute<C, 4, MT>(w, x, shift, acc);
-      if (j.kb == nkb_of(j.s) - 1) finish(j);
-    };
-    for (int i = 0; i < njobs; i += 2) {
-      consume(ja, wa, xa);
-      ja = advance(jb);
-      issue(ja, wa, xa);
-      if (i + 1 < njobs) consume(jb, wb, xb);
-      jb = advance(ja);
-      issue(jb, wb, xb);
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = tid; i < p.M * 4; i += blockDim.x) {
-      const int t = i >> 2, q = i & 3;
-      const int64_t row = (u >> 5) * 128 + (u & 31) + 32 * q;
-      if (row < p.H) {
-        float s = part[0][t][q];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) s += part[w][t][q];  // in wave order
-        const float sr = bf16_bits_to_f32(f32_to_bf16_bits(s));
-        p.out[static_cast<int64_t>(t) * p.H + row] = f32_to_bf16_bits(sr + ysh[t][q]);
+    if (tid < p.M * R) {
+      const int t = tid / R, q = tid % R;
+      if (rv[q]) {
+        float acc = 0.0f;
+        for (int j = 0; j < p.topk; ++j) acc += tws[t * p.topk + j] * yv[p.M + t * p.topk + j][q];
+        const float sr = bf16_bits_to_f32(f32_to_bf16_bits(acc));
+        p.out[static_cast<int64_t>(t) * p.H + rows[q]] = f32_to_bf16_bits(sr + yv[t][q]);
       }
     }
     __syncthreads();
@@ -962,8 +855,6 @@ __global__ __launch_bounds__(kMoeDownWaves * 64) void k_moe_down_mfma(const MoeD
 // ------------------------------------------------------------------ launch
 namespace {
 
-// Persistent gate_up workgroups: about five resident per CU.
-constexpr int64_t kMoeGateUpGrid = 1280;
 // Persistent MFMA gate_up workgroups: two per CU.
 constexpr int64_t kMoeMfmaGrid = 512;
 
@@ -972,42 +863,35 @@ constexpr int64_t kMoeMfmaGrid = 512;
 // dequant (measured on the 128-expert decode block).
 bool moe_use_mfma(int M) { return M >= 3; }
 
-template <int MT>
-hipError_t launch_gate_up_mt(const MoeGateUpParams& p, int c, hipStream_t stream) {
-  const int64_t max_items = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 32) + (p.SI + 127) / 128 * 32;
-  const dim3 grid(static_cast<unsigned>(max_items < kMoeGateUpGrid ? max_items : kMoeGateUpGrid)), block(256);
-  switch (c) {
-    case 1: hipLaunchKernelGGL((k_moe_gate_up<MT, 1>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_moe_gate_up<MT, 2>), grid, block, 0, stream, p); break;
-  }
+// The longest K (I or SI, in 8-k chunks) the one-block VALU down_combine
+// takes: 4 waves x 64 lanes x 2 chunks.
+constexpr int64_t kMoeDownPairsMaxChunks = 4 * 64 * 2;
+
+template <int NW, int CL, int SG>
+hipError_t launch_down_pairs_sg(const MoeDownParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((k_moe_down_pairs<NW, CL, SG>), grid, dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// Waves per down_combine workgroup (each takes every kMoeDownValuWaves-th slot).
-constexpr int kMoeDownValuWaves = 4;
-
-template <int MT>
-hipError_t launch_down_mt(const MoeDownParams& p, int c, hipStream_t stream) {
-  constexpr int NW = kMoeDownValuWaves;
-  const int64_t units = (p.H + 127) / 128 * 32;
-  const dim3 grid(static_cast<unsigned>(units < 4096 ? units : 4096)), block(NW * 64);
-  switch (c) {
-    case 1: hipLaunchKernelGGL((k_moe_down_combine<MT, 1, NW>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_moe_down_combine<MT, 2, NW>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((k_moe_down_combine<MT, 3, NW>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_moe_down_combine<MT, 4, NW>), grid, block, 0, stream, p); break;
+template <int NW, int CL>
+hipError_t launch_down_pairs_cl(const MoeDownParams& p, int sg, dim3 grid, hipStream_t stream) {
+  if constexpr (CL == 1) {
+    if (sg >= 9) return launch_down_pairs_sg<NW, CL, 9>(p, grid, stream);
+    if (sg >= 5) return launch_down_pairs_sg<NW, CL, 5>(p, grid, stream);
   }
-  return hipGetLastError();
+  if (sg >= 4) return launch_down_pairs_sg<NW, CL, 4>(p, grid, stream);
+  if (sg >= 2) return launch_down_pairs_sg<NW, CL, 2>(p, grid, stream);
+  return launch_down_pairs_sg<NW, CL, 1>(p, grid, stream);
 }
 
-// Chunk positions per lane: enough to cover K in one block where that fits
-// in `cmax`, else `cmax` and several K blocks.
-int chunks_per_lane(int64_t k, int64_t lanes, int cmax) {
-  const int64_t need = (k / 8 + lanes - 1) / lanes;
-  if (need <= 1) return 1;
-  if (need <= 2) return 2;
-  if (need <= 3 && cmax >= 3) return 3;
-  return cmax;
+hipError_t launch_down_pairs(const MoeDownParams& p, int nw, int cl, int sg, dim3 grid, hipStream_t stream) {
+  switch (nw * 10 + cl) {
+    case 11: return launch_down_pairs_cl<1, 1>(p, sg, grid, stream);
+    case 21: return launch_down_pairs_cl<2, 1>(p, sg, grid, stream);
+    case 31: return launch_down_pairs_cl<3, 1>(p, sg, grid, stream);
+    case 41: return launch_down_pairs_cl<4, 1>(p, sg, grid, stream);
+    default: return launch_down_pairs_cl<4, 2>(p, sg, grid, stream);
+  }
 }
 
 }  // namespace
@@ -1016,7 +900,7 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   const int pairs = p.M * p.topk;
   p.slots_max = pairs < p.E ? pairs : p.E;
   // (the VALU forms read a quad's scale words as one 16-byte chunk, and
-  // route at most kMoeValuMaxPairs pairs)
+  // take at most kMoeValuMaxPairs pairs)
   if (moe_use_mfma(p.M) || !p.scales16 || pairs > kMoeValuMaxPairs) {
     // one work unit per wave at least, two resident workgroups per CU at most
     const int64_t units = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 8) + (p.SI + 127) / 128 * 8;
@@ -1027,22 +911,43 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
     else hipLaunchKernelGGL((k_moe_gate_up_mfma<8>), grid, block, 0, stream, p);
     return hipGetLastError();
   }
-  const int c = chunks_per_lane(p.H, 4 * 64, 2);
-  if (p.M <= 1) return launch_gate_up_mt<1>(p, c, stream);
-  return launch_gate_up_mt<2>(p, c, stream);
+  // one item per workgroup (a persistent grid of 1280 or 2560 workgroups
+  // measured 1.6 / 3.7 us slower at one token); the 4 waves' 8-k chunks
+  // cover H in one block up to 2048 columns with one chunk per lane
+  const int64_t items = static_cast<int64_t>(pairs) * ((p.I + 127) / 128 * 32) + (p.SI + 127) / 128 * 32;
+  const dim3 grid(static_cast<unsigned>(items)), block(256);
+  const bool one = p.H / 8 <= 4 * 64;
+  if (p.M <= 1) {
+    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 2>), grid, block, 0, stream, p);
+  } else {
+    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 2>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
-  if (moe_use_mfma(p.M) || !p.scales16 || p.M * p.topk > kMoeValuMaxPairs) {
+  const int64_t nch = (p.I > p.SI ? p.I : p.SI) / 8;
+  // (rows of I or SI beyond kMoeDownPairsMaxChunks chunks also take the
+  // MFMA form, which runs any K)
+  if (moe_use_mfma(p.M) || !p.scales16 || p.M * p.topk > kMoeValuMaxPairs || nch > kMoeDownPairsMaxChunks) {
     const int64_t tiles = (p.H + 127) / 128 * 8;
     const dim3 grid(static_cast<unsigned>(tiles < 4096 ? tiles : 4096)), block(kMoeDownWaves * 64);
     if (p.M <= 4) hipLaunchKernelGGL((k_moe_down_mfma<4>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((k_moe_down_mfma<8>), grid, block, 0, stream, p);
     return hipGetLastError();
   }
-  const int64_t kmax = p.I > p.SI ? p.I : p.SI;
-  const int c = chunks_per_lane(kmax, 64, 4);
-  return launch_down_mt<1>(p, c, stream);
+  // waves and chunks per lane that cover the longer K in one block; SG jobs
+  // in flight at once, SG * CL * 6 loads (+3) within vmcnt's 63
+  const int nw = static_cast<int>(nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 192 ? 3 : 4);
+  const int cl = nch <= nw * 64 ? 1 : 2;
+  const int jobs = p.M + p.M * p.topk;
+  const int sg_max = cl == 1 ? 9 : 4;
+  const int sg = jobs < sg_max ? jobs : sg_max;
+  const int64_t units = (p.H + 127) / 128 * 32;
+  const dim3 grid(static_cast<unsigned>(units < 8192 ? units : 8192));
+  return launch_down_pairs(p, nw, cl, sg, grid, stream);
 }
 
 }  // namespace w4a16
