@@ -70,7 +70,7 @@ def log(*a):
 
 
 # the sources the dense GEMV kernels are compiled from
-GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp", "launch.hpp"]
+GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp", "chunk_core.hpp", "launch.hpp"]
 
 
 def source_digest(csrc: str | None = None) -> str:

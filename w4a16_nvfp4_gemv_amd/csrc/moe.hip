@@ -229,19 +229,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
   const rsrc_t rx = make_rsrc(p.x, static_cast<uint32_t>(p.M) * p.H * 2);
   const float gssh = *p.gssh;
 
-  auto run = [&](auto nt_tag, bool shared, int j, int u, int e, float scale) {
+  // UPQ: the up rows form aligned quads too (rows of an expert multiple of
+  // 128), so the scale loads need no branch
+  auto run = [&](auto nt_tag, auto upq_tag, bool shared, int j, int u) {
     constexpr int NT = decltype(nt_tag)::value;  // token rows of the item
+    constexpr bool UPQ = decltype(upq_tag)::value;
     constexpr int V = NT * 4 * PV;               // value index (m * 4 + q) * 2 + w
     using RS = ReduceScatter<V, PV>;
     const int half = shared ? p.SI : p.I;
     int64_t rows[8];
     bool rv[8];
     quad_rows<8>(u, half, half, rows, rv);
-    const bool quad_ok[2] = {true, half % 128 == 0};
-    const rsrc_t rw = uniform_rsrc(shared ? p.wsh : p.w1 + e * p.w1_expert_bytes,
-                                   static_cast<uint32_t>(shared ? p.wsh_bytes : p.w1_expert_bytes));
-    const rsrc_t rs = uniform_rsrc(shared ? p.ssh : p.w1s + e * p.s1_expert_bytes,
-                                   static_cast<uint32_t>(shared ? p.ssh_bytes : p.s1_expert_bytes));
+    const bool quad_ok[2] = {true, UPQ};
     uint32_t xoff[NT];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
@@ -253,6 +252,12 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int m = 0; m < NT; ++m) acc[i][m] = 0.0f;
+    const int e = shared ? 0 : clamp_expert(uniform(p.ids[j]), p.E);
+    const float scale = shared ? gssh : p.alpha[e];
+    const rsrc_t rw = uniform_rsrc(shared ? p.wsh : p.w1 + e * p.w1_expert_bytes,
+                                   static_cast<uint32_t>(shared ? p.wsh_bytes : p.w1_expert_bytes));
+    const rsrc_t rs = uniform_rsrc(shared ? p.ssh : p.w1s + e * p.s1_expert_bytes,
+                                   static_cast<uint32_t>(shared ? p.ssh_bytes : p.s1_expert_bytes));
     for (int kb = 0; kb < nkb; ++kb) {
       uint32_t ch[C];
       bool ok[C];
@@ -307,14 +312,17 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
     __syncthreads();
   };
 
+  using Aligned = std::true_type;
+  using Unaligned = std::false_type;
   for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
     if (item < units_s) {
-      run(std::integral_constant<int, MT>{}, true, 0, item, 0, gssh);
+      if (p.SI % 128 == 0) run(std::integral_constant<int, MT>{}, Aligned{}, true, 0, item);
+      else run(std::integral_constant<int, MT>{}, Unaligned{}, true, 0, item);
     } else {
       const int j = (item - units_s) / units_r;
       const int u = item - units_s - j * units_r;
-      const int e = clamp_expert(uniform(p.ids[j]), p.E);
-      run(std::integral_constant<int, 1>{}, false, j, u, e, p.alpha[e]);
+      if (p.I % 128 == 0) run(std::integral_constant<int, 1>{}, Aligned{}, false, j, u);
+      else run(std::integral_constant<int, 1>{}, Unaligned{}, false, j, u);
     }
   }
 }
@@ -349,9 +357,11 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
   const int J = p.M + P;
   // every pair's id, alpha2 and routing weight, issued first (vector loads:
   // the waits the compiler adds for them come after the shared jobs' loads)
-  const int my_e = lane < P ? clamp_expert(p.ids[lane], p.E) : 0;
-  const float my_tw = lane < P ? p.tw[lane] : 0.0f;
-  const float my_a2 = lane < P ? p.alpha2[my_e] : 0.0f;
+  // (unconditional loads: a branch around them would make the compiler wait
+  // for them inside it, before the shared jobs' loads)
+  const int my_id = p.ids[lane < P ? lane : 0];
+  const float my_tw = p.tw[lane < P ? lane : 0];
+  float my_a2 = 0.0f;  // loaded once the first jobs' loads are issued
   const float gssd = *p.gssd;
   const int64_t units = (p.H + 127) / 128 * 32;
   const uint32_t shift = 8u * ((lane >> 1) & 3);
@@ -373,7 +383,8 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
         const bool valid = j < J;
         const bool shared = j < p.M;
         const int pair = shared ? 0 : (valid ? j - p.M : 0);
-        const int e = shared ? 0 : __builtin_amdgcn_readlane(my_e, pair);
+        int e = 0;
+        if (!shared) e = clamp_expert(__builtin_amdgcn_readlane(my_id, pair), p.E);  // (no wait for the ids in shared jobs)
         const int k = shared ? p.SI : p.I;
         const uint32_t nch = k / 8;
         uint32_t ch[CL];
@@ -395,6 +406,7 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
         chunk_issue_w<CL, R>(wb[s], uniform_rsrc(wbase, wbytes), k / 2, uniform_rsrc(sbase, sbytes), k / 64, rows, rv,
                              quad_ok, ch, ok);
       }
+      if (!tw_stored) my_a2 = p.alpha2[clamp_expert(my_id, p.E)];
       __builtin_amdgcn_sched_barrier(0);  // every load of the group ahead of the arithmetic
       float v[V];
 #pragma unroll
