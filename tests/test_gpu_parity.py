@@ -600,10 +600,11 @@ def test_moe_small_shapes(m, e, topk, h, inter, si):
 @pytest.mark.parametrize("m,ids", [
     (1, [[3, 3, 1, 3]]),
     (2, [[0, 5, 0, 2], [5, 5, 5, 5]]),
+    (4, [[1, 2, 3, 4], [4, 3, 2, 1], [0, 0, 5, 5], [2, 2, 2, 2]]),
 ])
-def test_moe_duplicate_experts_one_or_two_tokens(m, ids):
-    """One or two tokens (the forms with one job per pair): pairs routed to
-    the same expert, within a token and across the two tokens."""
+def test_moe_duplicate_experts_up_to_four_tokens(m, ids):
+    """Up to four tokens (the forms with one job per pair): pairs routed to
+    the same expert, within a token and across tokens."""
     e, topk, h, inter, si = 6, 4, 256, 192, 128
     wts = synth.moe_weights(e, h, inter, si, seed=353 + m)
     tok = synth.moe_tokens(m, h, e, topk, seed=354 + m)
@@ -613,7 +614,7 @@ def test_moe_duplicate_experts_one_or_two_tokens(m, ids):
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe duplicates M={m}")
 
 
-@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("m", [1, 2, 4])
 @pytest.mark.parametrize("h,inter,si", [
     (128, 512, 64),       # down_combine: one wave
     (192, 1024, 512),     # two waves
@@ -622,7 +623,7 @@ def test_moe_duplicate_experts_one_or_two_tokens(m, ids):
     (4160, 1024, 1024),   # gate_up: two chunks per lane, two K blocks
     (128, 4160, 64),      # I beyond the one-block down_combine: the MFMA form
 ])
-def test_moe_one_or_two_tokens_k_extents(m, h, inter, si):
+def test_moe_up_to_four_tokens_k_extents(m, h, inter, si):
     """The K extents that select the waves and chunks of the one-job-per-pair
     forms (and the fallback past them), top-8 of 16 experts."""
     e, topk = 16, 8
@@ -631,6 +632,18 @@ def test_moe_one_or_two_tokens_k_extents(m, h, inter, si):
     _say("moe K extents", m, h, inter, si)
     act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe K extents M={m} H={h} I={inter} SI={si}")
+
+
+@pytest.mark.parametrize("m,topk", [(4, 16), (5, 16)])
+def test_moe_most_pairs_of_the_pair_forms(m, topk):
+    """64 pairs (4 tokens x 16): the most the one-job-per-pair forms take;
+    5 tokens go to the MFMA forms."""
+    e, h, inter, si = 24, 256, 128, 192
+    wts = synth.moe_weights(e, h, inter, si, seed=357 + m)
+    tok = synth.moe_tokens(m, h, e, topk, seed=358 + m)
+    _say("moe pair-form pairs", m, topk)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), f"moe pairs M={m} topk={topk}")
 
 
 def test_moe_duplicate_experts_within_a_token():

@@ -8,7 +8,7 @@
 //
 // Two forms of each kernel:
 //
-// VALU forms (M <= 2).  One job per pair: a job reads the weights of its
+// VALU forms (M <= 4).  One job per pair: a job reads the weights of its
 // pair's expert (two pairs routed to one expert read them twice, the second
 // time mostly from L2), so no routing table is built and a workgroup needs
 // only the ids of its jobs.  Chunk-interleaved loads and per-token dot
@@ -17,7 +17,7 @@
 // waves split H; down_combine gives a workgroup a quad of H rows and puts
 // the loads of up to 9 jobs in flight at once.
 //
-// MFMA forms (M >= 3), expert-major: every routed expert's weights are read
+// MFMA forms (M >= 5), expert-major: every routed expert's weights are read
 // once per call, for all the tokens routed to it.  Every workgroup rebuilds
 // the call's routing in LDS from ids (at most 32 tokens x 16 slots = 512
 // pairs): the distinct experts in order of first appearance ("slots"), and
@@ -93,8 +93,13 @@ struct alignas(16) MoeRouting {
   int32_t D;                        // distinct experts
 };
 
-// Pairs the VALU forms (one or two tokens) take: at most 2 x 16.
-constexpr int kMoeValuMaxPairs = 32;
+// Tokens and pairs the VALU forms take (one job per pair).  Measured on the
+// 128-expert decode block against the MFMA forms (us, gate_up / down_combine):
+// 3 tokens 42.9 / 25.1 against 53.2 / 27.4, 4 tokens 53.4 / 32.3 against
+// 56.8 / 32.0; at 6 and 8 tokens the VALU forms were slower (gate_up 129 /
+// 163 against 77 / 95).
+constexpr int kMoeValuMaxTokens = 4;
+constexpr int kMoeValuMaxPairs = 64;
 
 // Number of i in [lo, hi) with a[i] == v: a scan of an LDS array in blocks of
 // 16 entries read as four 16-byte broadcasts (the array is readable up to
@@ -201,7 +206,7 @@ __device__ void build_routing(MoeRouting& r, const int32_t* ids, const float* tw
 }
 
 // ------------------------------------------------------------------ gate_up, one job per pair
-// One or two tokens: items are (shared expert, quad of SI rows) -- first,
+// Up to four tokens: items are (shared expert, quad of SI rows) -- first,
 // since they need no id -- and (pair j, quad of I rows) for every pair, so
 // a workgroup needs only the id of its item's pair, read by one scalar-
 // uniform load, and no routing table.  Two pairs routed to one expert read
@@ -213,7 +218,7 @@ template <int MT, int C>
 __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams p) {
   constexpr int KS = 4;                 // waves per item, each a slice of H
   constexpr int PV = 2;                 // gate, up
-  __shared__ float red[KS - 1][MT * 4 * PV][64];
+  __shared__ float red[KS - 1][MT * 4 * PV / 4][64];  // the values left per lane by the reduce-scatter
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kw = uniform(tid >> 6);
@@ -319,8 +324,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
       if (p.SI % 128 == 0) run(std::integral_constant<int, MT>{}, Aligned{}, true, 0, item);
       else run(std::integral_constant<int, MT>{}, Unaligned{}, true, 0, item);
     } else {
-      const int j = (item - units_s) / units_r;
-      const int u = item - units_s - j * units_r;
+      // unit-major: the pairs of one expert read the same rows at about the
+      // same time, the second read from L2
+      const int u = (item - units_s) / P;
+      const int j = item - units_s - u * P;
       if (p.I % 128 == 0) run(std::integral_constant<int, 1>{}, Aligned{}, false, j, u);
       else run(std::integral_constant<int, 1>{}, Unaligned{}, false, j, u);
     }
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
 }
 
 // ------------------------------------------------------------------ down_combine, one job per pair
-// One or two tokens: the work of a quad of H rows is P + M jobs, the shared
+// Up to four tokens: the work of a quad of H rows is P + M jobs, the shared
 // expert for each token and then every pair in order (pair j reads the
 // weights of expert ids[j] and its own act row; two pairs routed to one
 // expert read its weights twice, the second time from L2).  No routing table
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
 // and waves, rounded to BF16 (y_j = bf16(acc * alpha2[e_j]), y_shared =
 // bf16(acc * gssd)), and the combine adds tw_j * y_j over j in ascending
 // order in FP32 before the two BF16 roundings of the moe_gemv page.
-constexpr int kMoeDownPairsMaxJobs = kMoeValuMaxPairs + 2;
+constexpr int kMoeDownPairsMaxJobs = kMoeValuMaxPairs + kMoeValuMaxTokens;
 
 template <int NW, int CL, int SG>
 __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams p) {
@@ -870,10 +877,9 @@ namespace {
 // Persistent MFMA gate_up workgroups: two per CU.
 constexpr int64_t kMoeMfmaGrid = 512;
 
-// The MFMA forms from three tokens up; one or two tokens keep the VALU
-// forms, whose per-token dot products then cost no more than the MFMA path's
-// dequant (measured on the 128-expert decode block).
-bool moe_use_mfma(int M) { return M >= 3; }
+// The MFMA forms from five tokens up: below, the VALU forms' per-token dot
+// products cost no more than the MFMA path's dequant (kMoeValuMaxTokens).
+bool moe_use_mfma(int M) { return M > kMoeValuMaxTokens; }
 
 // The longest K (I or SI, in 8-k chunks) the one-block VALU down_combine
 // takes: 4 waves x 64 lanes x 2 chunks.
@@ -932,9 +938,12 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   if (p.M <= 1) {
     if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 1>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 2>), grid, block, 0, stream, p);
-  } else {
+  } else if (p.M <= 2) {
     if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 1>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 2>), grid, block, 0, stream, p);
+  } else {
+    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<4, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_moe_gate_up_pairs<4, 2>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
