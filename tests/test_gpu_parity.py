@@ -614,7 +614,7 @@ def test_moe_duplicate_experts_up_to_four_tokens(m, ids):
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe duplicates M={m}")
 
 
-@pytest.mark.parametrize("m", [1, 2, 4])
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
 @pytest.mark.parametrize("h,inter,si", [
     (128, 512, 64),       # down_combine: one wave
     (192, 1024, 512),     # two waves
@@ -634,10 +634,11 @@ def test_moe_up_to_four_tokens_k_extents(m, h, inter, si):
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe K extents M={m} H={h} I={inter} SI={si}")
 
 
-@pytest.mark.parametrize("m,topk", [(4, 16), (5, 16)])
+@pytest.mark.parametrize("m,topk", [(4, 16), (5, 16), (8, 16), (9, 16)])
 def test_moe_most_pairs_of_the_pair_forms(m, topk):
-    """64 pairs (4 tokens x 16): the most the one-job-per-pair forms take;
-    5 tokens go to the MFMA forms."""
+    """The token counts around the limits of the one-job-per-pair forms:
+    down_combine takes up to 4 tokens (64 pairs), gate_up up to 8 (128
+    pairs); beyond, the MFMA forms."""
     e, h, inter, si = 24, 256, 128, 192
     wts = synth.moe_weights(e, h, inter, si, seed=357 + m)
     tok = synth.moe_tokens(m, h, e, topk, seed=358 + m)

@@ -8,16 +8,16 @@
 //
 // Two forms of each kernel:
 //
-// VALU forms (M <= 4).  One job per pair: a job reads the weights of its
-// pair's expert (two pairs routed to one expert read them twice, the second
-// time mostly from L2), so no routing table is built and a workgroup needs
-// only the ids of its jobs.  Chunk-interleaved loads and per-token dot
-// products (chunk_core.hpp).  gate_up gives every (shared expert or pair,
-// quad of gate rows and the matching up rows) item a workgroup whose four
-// waves split H; down_combine gives a workgroup a quad of H rows and puts
-// the loads of up to 9 jobs in flight at once.
+// VALU forms (gate_up up to 8 tokens, down_combine up to 4).  One job per
+// pair: a job reads the weights of its pair's expert (two pairs routed to one
+// expert read them twice, the second time mostly from L2), so no routing
+// table is built and a workgroup needs only the ids of its jobs.
+// Chunk-interleaved loads and per-token dot products (chunk_core.hpp).
+// gate_up gives every (token, shared-expert quad) and (pair, routed quad)
+// item a workgroup whose four waves split H; down_combine gives a workgroup
+// a quad of H rows and puts the loads of up to 9 jobs in flight at once.
 //
-// MFMA forms (M >= 5), expert-major: every routed expert's weights are read
+// MFMA forms (above those token counts), expert-major: every routed expert's weights are read
 // once per call, for all the tokens routed to it.  Every workgroup rebuilds
 // the call's routing in LDS from ids (at most 32 tokens x 16 slots = 512
 // pairs): the distinct experts in order of first appearance ("slots"), and
@@ -93,13 +93,16 @@ struct alignas(16) MoeRouting {
   int32_t D;                        // distinct experts
 };
 
-// Tokens and pairs the VALU forms take (one job per pair).  Measured on the
-// 128-expert decode block against the MFMA forms (us, gate_up / down_combine):
-// 3 tokens 42.9 / 25.1 against 53.2 / 27.4, 4 tokens 53.4 / 32.3 against
-// 56.8 / 32.0; at 6 and 8 tokens the VALU forms were slower (gate_up 129 /
-// 163 against 77 / 95).
-constexpr int kMoeValuMaxTokens = 4;
-constexpr int kMoeValuMaxPairs = 64;
+// Tokens the VALU forms (one job per pair) take, measured on the 128-expert
+// decode block against the MFMA forms (us):
+//   gate_up       4 / 6 / 8 tokens 47.2 / 66.8 / 87.3 against 55.0 / 77.0 /
+//                 94.8; 16 / 32 tokens 172 / 337 against 152 / 209
+//   down_combine  3 / 4 tokens 25.1 / 32.3 against 27.3 / 32.0; 6 / 8 tokens
+//                 47.3 / 61.4 against 43.6 / 54.5
+constexpr int kMoeGateUpPairsMaxTokens = 8;
+constexpr int kMoeDownPairsMaxTokens = 4;
+// down_combine keeps one pair per lane of a wave
+constexpr int kMoeDownPairsMaxPairs = 64;
 
 // Number of i in [lo, hi) with a[i] == v: a scan of an LDS array in blocks of
 // 16 entries read as four 16-byte broadcasts (the array is readable up to
@@ -206,26 +209,30 @@ __device__ void build_routing(MoeRouting& r, const int32_t* ids, const float* tw
 }
 
 // ------------------------------------------------------------------ gate_up, one job per pair
-// Up to four tokens: items are (shared expert, quad of SI rows) -- first,
-// since they need no id -- and (pair j, quad of I rows) for every pair, so
-// a workgroup needs only the id of its item's pair, read by one scalar-
-// uniform load, and no routing table.  Two pairs routed to one expert read
-// its weights twice (the second time mostly from L2).  An item reads its
-// gate and up quads once and applies them to its tokens (the pair's token,
-// or all M tokens for the shared expert) with the chunked VALU core; the 4
-// waves split H.
-template <int MT, int C>
+// Up to kMoeGateUpPairsMaxTokens tokens: every item is one token's product
+// with one quad of gate rows and the matching up rows -- (token t, quad of
+// the shared expert's SI rows) first, since they need no id, then (pair j,
+// quad of I rows), unit-major, so that the pairs routed to one expert read
+// the same rows at about the same time and all but the first read them from
+// L2.  A workgroup needs only the id of its item's pair, read by one
+// scalar-uniform load, and no routing table.  The 4 waves split H with the
+// chunked VALU core (one token per item: the registers of more tokens cost
+// more waves per SIMD than the shared reads save).
+template <int C>
 __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams p) {
   constexpr int KS = 4;                 // waves per item, each a slice of H
   constexpr int PV = 2;                 // gate, up
-  __shared__ float red[KS - 1][MT * 4 * PV / 4][64];  // the values left per lane by the reduce-scatter
+  constexpr int V = 4 * PV;             // value index q * 2 + w
+  using RS = ReduceScatter<V, PV>;
+  __shared__ float red[KS - 1][RS::LEFT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kw = uniform(tid >> 6);
   const int P = p.M * p.topk;
   const int units_r = (p.I + 127) / 128 * 32;
   const int units_s = (p.SI + 127) / 128 * 32;
-  const int items = P * units_r + units_s;
+  const int items_s = p.M * units_s;
+  const int items = P * units_r + items_s;
   const uint32_t nch = p.H / 8;
   const int nkb = static_cast<int>((nch + KS * C * 64 - 1) / (KS * C * 64));
   const uint32_t shift = 8u * ((lane >> 1) & 3);
@@ -234,29 +241,21 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
   const rsrc_t rx = make_rsrc(p.x, static_cast<uint32_t>(p.M) * p.H * 2);
   const float gssh = *p.gssh;
 
-  // UPQ: the up rows form aligned quads too (rows of an expert multiple of
-  // 128), so the scale loads need no branch
-  auto run = [&](auto nt_tag, auto upq_tag, bool shared, int j, int u) {
-    constexpr int NT = decltype(nt_tag)::value;  // token rows of the item
+  // t: the item's token; j: its pair (routed items).  UPQ: the up rows form
+  // aligned quads too (rows of an expert a multiple of 128), so the scale
+  // loads need no branch (as a runtime branch it split the loads, and the
+  // compiler waited for some of them before issuing the rest)
+  auto run = [&](auto upq_tag, bool shared, int t, int j, int u) {
     constexpr bool UPQ = decltype(upq_tag)::value;
-    constexpr int V = NT * 4 * PV;               // value index (m * 4 + q) * 2 + w
-    using RS = ReduceScatter<V, PV>;
     const int half = shared ? p.SI : p.I;
     int64_t rows[8];
     bool rv[8];
     quad_rows<8>(u, half, half, rows, rv);
     const bool quad_ok[2] = {true, UPQ};
-    uint32_t xoff[NT];
+    const uint32_t xoff[1] = {static_cast<uint32_t>(t) * p.H * 2};
+    float acc[8][1];
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-      const int t = shared ? m : j / p.topk;
-      xoff[m] = off_if(shared ? m < p.M : true, static_cast<uint32_t>(t) * p.H * 2);
-    }
-    float acc[8][NT];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int m = 0; m < NT; ++m) acc[i][m] = 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i][0] = 0.0f;
     const int e = shared ? 0 : clamp_expert(uniform(p.ids[j]), p.E);
     const float scale = shared ? gssh : p.alpha[e];
     const rsrc_t rw = uniform_rsrc(shared ? p.wsh : p.w1 + e * p.w1_expert_bytes,
@@ -271,20 +270,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
         ch[q] = static_cast<uint32_t>((kb * KS + kw) * C + q) * 64 + lane;
         ok[q] = ch[q] < nch;
       }
-      ChunkX<C, NT> xb;
+      ChunkX<C, 1> xb;
       ChunkW<C, 8> wb;
-      chunk_issue_x<C, NT>(xb, rx, xoff, ch, ok);
+      chunk_issue_x<C, 1>(xb, rx, xoff, ch, ok);
       chunk_issue_w<C, 8>(wb, rw, row_bytes, rs, tiles, rows, rv, quad_ok, ch, ok);
       __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
-      chunk_compute<C, 8, NT>(wb, xb, shift, acc);
+      chunk_compute<C, 8, 1>(wb, xb, shift, acc);
     }
     float v[V];
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int w = 0; w < PV; ++w) v[(m * 4 + q) * PV + w] = acc[4 * w + q][m];
+      for (int w = 0; w < PV; ++w) v[q * PV + w] = acc[4 * w + q][0];
     reduce_scatter<V, PV>(v);
     if (kw > 0) {
 #pragma unroll
@@ -299,15 +296,14 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
       const int base = reduce_scatter_base<V, PV>(lane);
 #pragma unroll
       for (int i = 0; i < RS::LEFT / PV; ++i) {
-        const int vi = base + i * PV;
-        const int m = vi / (4 * PV), q = (vi / PV) % 4;
+        const int q = (base + i * PV) / PV;
         const int64_t row = static_cast<int64_t>(u >> 5) * 128 + (u & 31) + 32 * q;
-        if ((lane & 15) == i && row < half && (!shared || m < p.M)) {
+        if ((lane & 15) == i && row < half) {
           float g = v[i * PV] * scale, up = v[i * PV + 1] * scale;
           if (shared) {
             g = bf16_bits_to_f32(f32_to_bf16_bits(g));
             up = bf16_bits_to_f32(f32_to_bf16_bits(up));
-            p.sact[static_cast<int64_t>(m) * p.SI + row] = f32_to_bf16_bits(silu_f32(g) * up);
+            p.sact[static_cast<int64_t>(t) * p.SI + row] = f32_to_bf16_bits(silu_f32(g) * up);
           } else {
             p.act[static_cast<int64_t>(j) * p.I + row] = f32_to_bf16_bits(silu_f32(g) * up);
           }
@@ -317,19 +313,17 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
     __syncthreads();
   };
 
-  using Aligned = std::true_type;
-  using Unaligned = std::false_type;
   for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
-    if (item < units_s) {
-      if (p.SI % 128 == 0) run(std::integral_constant<int, MT>{}, Aligned{}, true, 0, item);
-      else run(std::integral_constant<int, MT>{}, Unaligned{}, true, 0, item);
+    if (item < items_s) {
+      const int t = item / units_s;
+      const int u = item - t * units_s;
+      if (p.SI % 128 == 0) run(std::true_type{}, true, t, 0, u);
+      else run(std::false_type{}, true, t, 0, u);
     } else {
-      // unit-major: the pairs of one expert read the same rows at about the
-      // same time, the second read from L2
-      const int u = (item - units_s) / P;
-      const int j = item - units_s - u * P;
-      if (p.I % 128 == 0) run(std::integral_constant<int, 1>{}, Aligned{}, false, j, u);
-      else run(std::integral_constant<int, 1>{}, Unaligned{}, false, j, u);
+      const int u = (item - items_s) / P;
+      const int j = item - items_s - u * P;
+      if (p.I % 128 == 0) run(std::true_type{}, false, j / p.topk, j, u);
+      else run(std::false_type{}, false, j / p.topk, j, u);
     }
   }
 }
@@ -346,7 +340,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
 // and waves, rounded to BF16 (y_j = bf16(acc * alpha2[e_j]), y_shared =
 // bf16(acc * gssd)), and the combine adds tw_j * y_j over j in ascending
 // order in FP32 before the two BF16 roundings of the moe_gemv page.
-constexpr int kMoeDownPairsMaxJobs = kMoeValuMaxPairs + kMoeValuMaxTokens;
+constexpr int kMoeDownPairsMaxJobs = kMoeDownPairsMaxPairs + kMoeDownPairsMaxTokens;
 
 template <int NW, int CL, int SG>
 __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams p) {
@@ -355,8 +349,8 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
   using RS = ReduceScatter<V, 1>;
   __shared__ float red[NW][V];
   __shared__ float yv[kMoeDownPairsMaxJobs][R];  // jobs 0..M-1: shared expert, then pairs
-  __shared__ float tws[kMoeValuMaxPairs];
-  __shared__ float a2s[kMoeValuMaxPairs];
+  __shared__ float tws[kMoeDownPairsMaxPairs];
+  __shared__ float a2s[kMoeDownPairsMaxPairs];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -877,9 +871,6 @@ namespace {
 // Persistent MFMA gate_up workgroups: two per CU.
 constexpr int64_t kMoeMfmaGrid = 512;
 
-// The MFMA forms from five tokens up: below, the VALU forms' per-token dot
-// products cost no more than the MFMA path's dequant (kMoeValuMaxTokens).
-bool moe_use_mfma(int M) { return M > kMoeValuMaxTokens; }
 
 // The longest K (I or SI, in 8-k chunks) the one-block VALU down_combine
 // takes: 4 waves x 64 lanes x 2 chunks.
@@ -917,9 +908,8 @@ hipError_t launch_down_pairs(const MoeDownParams& p, int nw, int cl, int sg, dim
 hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   const int pairs = p.M * p.topk;
   p.slots_max = pairs < p.E ? pairs : p.E;
-  // (the VALU forms read a quad's scale words as one 16-byte chunk, and
-  // take at most kMoeValuMaxPairs pairs)
-  if (moe_use_mfma(p.M) || !p.scales16 || pairs > kMoeValuMaxPairs) {
+  // (the VALU form reads a quad's scale words as one 16-byte chunk)
+  if (p.M > kMoeGateUpPairsMaxTokens || !p.scales16) {
     // one work unit per wave at least, two resident workgroups per CU at most
     const int64_t units = static_cast<int64_t>(p.slots_max) * ((p.I + 127) / 128 * 8) + (p.SI + 127) / 128 * 8;
     int64_t blocks = (units + kMoeGateUpWaves - 1) / kMoeGateUpWaves;
@@ -932,19 +922,11 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
   // one item per workgroup (a persistent grid of 1280 or 2560 workgroups
   // measured 1.6 / 3.7 us slower at one token); the 4 waves' 8-k chunks
   // cover H in one block up to 2048 columns with one chunk per lane
-  const int64_t items = static_cast<int64_t>(pairs) * ((p.I + 127) / 128 * 32) + (p.SI + 127) / 128 * 32;
+  const int64_t items =
+      static_cast<int64_t>(pairs) * ((p.I + 127) / 128 * 32) + static_cast<int64_t>(p.M) * ((p.SI + 127) / 128 * 32);
   const dim3 grid(static_cast<unsigned>(items)), block(256);
-  const bool one = p.H / 8 <= 4 * 64;
-  if (p.M <= 1) {
-    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 1>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_moe_gate_up_pairs<1, 2>), grid, block, 0, stream, p);
-  } else if (p.M <= 2) {
-    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 1>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_moe_gate_up_pairs<2, 2>), grid, block, 0, stream, p);
-  } else {
-    if (one) hipLaunchKernelGGL((k_moe_gate_up_pairs<4, 1>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_moe_gate_up_pairs<4, 2>), grid, block, 0, stream, p);
-  }
+  if (p.H / 8 <= 4 * 64) hipLaunchKernelGGL((k_moe_gate_up_pairs<1>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((k_moe_gate_up_pairs<2>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -952,7 +934,8 @@ hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
   const int64_t nch = (p.I > p.SI ? p.I : p.SI) / 8;
   // (rows of I or SI beyond kMoeDownPairsMaxChunks chunks also take the
   // MFMA form, which runs any K)
-  if (moe_use_mfma(p.M) || !p.scales16 || p.M * p.topk > kMoeValuMaxPairs || nch > kMoeDownPairsMaxChunks) {
+  if (p.M > kMoeDownPairsMaxTokens || !p.scales16 || p.M * p.topk > kMoeDownPairsMaxPairs ||
+      nch > kMoeDownPairsMaxChunks) {
     const int64_t tiles = (p.H + 127) / 128 * 8;
     const dim3 grid(static_cast<unsigned>(tiles < 4096 ? tiles : 4096)), block(kMoeDownWaves * 64);
     if (p.M <= 4) hipLaunchKernelGGL((k_moe_down_mfma<4>), grid, block, 0, stream, p);
