@@ -59,6 +59,7 @@ METRIC = "µs/call and achieved HBM GB/s (% of MI355X peak) at M=1,8,32"
 PEAK_GBPS = 8000.0
 SWEEP_M = [1, 2, 4, 8, 16, 32]
 SHAPES = [(4096, 4096, 0), (6144, 4096, 1)]
+SILU_N, SILU_K = 2 * 14336, 4096  # the fused gate|up silu workload
 COPY_SETS = 10  # step graphs; each reads 6 fresh copies of each weight
 COUNTER_LAUNCHES = 4
 CALIB_BYTES = 64 << 20
@@ -283,6 +284,35 @@ def floor_launcher(rf, torch, dev, ws, ss, w_bytes: int, s_bytes: int):
     return launch
 
 
+def silu_counter_pass() -> int:
+    """The fused gate|up silu GEMV at one token on its 28672 x 4096 weight,
+    launched 10 times, then the streaming-read reference over the same weight
+    and scale bytes 10 times: a short program for counter runs that compare
+    the two (rocprofv3 --pmc ... -- python3 bench.py --silu-counter-pass)."""
+    import torch
+
+    import synth
+    from w4a16_nvfp4_gemv_amd import _lib
+
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, k = SILU_N, SILU_K
+    d = synth.dense_w4a16(1, n, k, seed=synth.seed_for(2, 1))
+    x, w, s, gs = (d[key].to(dev) for key in ("x", "w", "s", "gs"))
+    out = torch.empty((1, n // 2), dtype=torch.bfloat16, device=dev)
+    h = torch.cuda.current_stream().cuda_stream
+    for _ in range(10):
+        if lib.nvfp4_gemv(x.data_ptr(), 1, k, k, w.data_ptr(), s.data_ptr(), gs.data_ptr(), n, 1, out.data_ptr(), h):
+            raise RuntimeError(f"nvfp4_gemv failed: {lib.w4a16_last_error().decode()}")
+    launch = floor_launcher(read_floor_lib(), torch, dev, [w], [s], n * k // 2, synth.flat_scale_bytes(n, k))
+    for i in range(10):
+        launch(i, h)
+    torch.cuda.synchronize()
+    log("silu counter pass done")
+    return 0
+
+
 def read_floor_mode() -> int:
     """Times the streaming-read reference alone: the weight + scale bytes of
     every call shape of the benchmark and a sweep of sizes, each over rotating
@@ -469,6 +499,7 @@ def main() -> int:
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--dispatch-table", action="store_true")
     ap.add_argument("--read-floor", action="store_true")
+    ap.add_argument("--silu-counter-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
@@ -480,6 +511,8 @@ def main() -> int:
         return dispatch_table()
     if args.read_floor:
         return read_floor_mode()
+    if args.silu_counter_pass:
+        return silu_counter_pass()
 
     import torch
 
@@ -681,7 +714,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
     budget = 600e6  # bytes of rotating weight copies per shape
 
     # fused gate|up SiLU GEMV, N = 2 x 14336, K = 4096
-    n, k = 2 * 14336, 4096
+    n, k = SILU_N, SILU_K
     base = synth.dense_w4a16(1, n, k, seed=synth.seed_for(2, 1))
     nc = max(2, int(budget // (n * k // 2)))
     ws = [base["w"].to(dev) for _ in range(nc)]
