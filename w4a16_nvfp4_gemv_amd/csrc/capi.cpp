@@ -120,7 +120,7 @@ int run_gemv(bool fp4, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, con
     q.x_bytes = static_cast<uint32_t>(((mc - 1) * ldx + K) * 2);
     q.out = out + m0 * n_out;
     q.M = static_cast<int>(mc);
-    const int path = s16 ? w4a16::choose_gemv_path(fp4, mc, N, K) : w4a16::kPathMfma;
+    const int path = s16 ? w4a16::choose_gemv_path(fp4, mc, N, K, silu_mul) : w4a16::kPathMfma;
     const int st2 = hip_status(w4a16::launch_gemv(fp4, q, silu_mul, path, static_cast<hipStream_t>(stream)));
     if (st2 != W4A16_OK) return st2;
   }
@@ -157,7 +157,7 @@ const char* gemv_kernel_name_of(int weight_fp4, int64_t M, int64_t N, int64_t K,
     p.part = reinterpret_cast<float*>(uintptr_t(256));
     p.cnt = reinterpret_cast<uint32_t*>(uintptr_t(256));
   }
-  w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, m_launch, N, K), name, sizeof name);
+  w4a16::describe_gemv(fp4, p, silu_mul, w4a16::choose_gemv_path(fp4, m_launch, N, K, silu_mul), name, sizeof name);
   ok();
   return name;
 }

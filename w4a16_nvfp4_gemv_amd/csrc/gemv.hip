@@ -1,11 +1,16 @@
 // Dense small-M GEMV kernels for gfx950: out = bf16(fp32(x @ W^T) * gs).
 //
-// Three kernel families serve the same entry points:
+// Four kernel families serve the same entry points:
 //   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns and M <= 2 tokens
-//     (up to 4 when the VALU path is forced).  VALU dot products over exactly
-//     decoded BF16 pairs (v_dot2_f32_bf16); lanes own interleaved 8-k chunks
-//     so that every load instruction of a wave reads one contiguous stretch,
-//     and a permlane reduce-scatter sums the lanes.
+//     (one token without silu_mul; up to 4 when the VALU path is forced).
+//     VALU dot products over exactly decoded BF16 pairs (v_dot2_f32_bf16);
+//     lanes own interleaved 8-k chunks so that every load instruction of a
+//     wave reads one contiguous stretch, and a permlane reduce-scatter sums
+//     the lanes.
+//   * k_gemv_blk -- NVFP4 without silu_mul, 2..4 tokens, rows of up to 4096
+//     columns: the same streaming as k_gemv_vchunk (256 contiguous bytes of a
+//     row per load, every load issued up front), with the products on
+//     v_mfma_f32_4x4x4_16b_bf16, whose 16 blocks take 16 k ranges of 4 rows.
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
 //     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 beyond
 //     8192 columns and NVFP4 rows longer than 16384 columns at M <= 2.
@@ -437,6 +442,206 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
         const float up = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P + 1] * gs));
         p.out[m * static_cast<int64_t>(p.half) + row] = f32_to_bf16_bits(silu_f32(g) * up);
       }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 4x4 block MFMA (NVFP4, M <= 8)
+// v_mfma_f32_4x4x4_16b_bf16 computes 16 independent 4x4x4 products, block
+// b on lanes 4b..4b+3: lane 4b+i holds row i of block b's A (4 k), lane
+// 4b+j column j of its B, and the result C[i][j] lands in item i of lane
+// 4b+j.  Here the 16 blocks are 16 k ranges of the same rows, so a unit of
+// quads {r, r+32, r+64, r+96} streams like the VALU kernel: lane 4b+j loads
+// 16 bytes of row j at byte 16b of a 256-byte stretch (one load of the wave
+// reads 256 contiguous bytes of each of the 4 rows), i.e. 32 codes, k =
+// 512s + 32b .. +31 of 512-k segment s.  Those codes are the B operand of 8
+// MFMAs (4 k each) against the A operand of tokens 4g..4g+3 (lane 4b+i:
+// token 4g+i, the same 32 k: 64 contiguous activation bytes).  Each MFMA
+// chain covers 16 k, one E4M3 block, and is scaled once into the FP32
+// accumulator, as the VALU kernel scales its chunk sums; the 16 blocks are
+// added across lanes at the end.  NQ quads per unit (2: rows r and r + 1 of
+// each quad position, whose scale chunks share a cache line), G groups of 4
+// tokens, C segments per lane, KS waves splitting K.  All loads are issued
+// up front.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_4x4x4(u32x2 a, u32x2 b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0,
+                                                0);
+}
+
+template <int G, int NQ, int C, int KS>
+__global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
+  constexpr int V = NQ * G * 4;  // values per lane: v = (q * G + g) * 4 + i
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kw = wave % KS;
+  const int64_t unit = static_cast<int64_t>(xcd_logical_block()) * (4 / KS) + wave / KS;
+  const int jr = lane & 3;   // row of the quad (B column) / token of the group (A row)
+  const int blk = lane >> 2;  // k range
+  const uint32_t row_bytes = p.K / 2;
+  const uint32_t ldx_bytes = static_cast<uint32_t>(p.ldx) * 2;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rs = make_rsrc(p.s, p.s_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+  const float gs = *p.gs;
+
+  // this lane's row in each quad of the unit
+  int64_t row[NQ];
+  bool rv[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t qi = unit * NQ + q;
+    row[q] = (qi >> 5) * 128 + (qi & 31) + 32 * jr;
+    rv[q] = row[q] < p.N && unit < p.units;
+  }
+  uint32_t k0[C];
+  bool kv[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    k0[c] = static_cast<uint32_t>(kw * C + c) * 512 + 32 * blk;
+    kv[c] = k0[c] < static_cast<uint32_t>(p.K);
+  }
+
+  // This wave's activations: token t (< 4G) of segment c at chunk t * XS + c * 64 of
+  // its LDS area, 1 KB per load; XS = 64C + 1 chunks per token, so the 16 lanes
+  // of one ds_read_b128 pass (4 tokens, 4 k ranges 64 bytes apart) hit distinct banks.
+  constexpr int XS = 64 * C + 1;
+  __shared__ u32x4 xl[4][4 * G * XS];
+  u32x4* xw = xl[wave];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ks = static_cast<uint32_t>(kw * C + c) * 512 + 8 * lane;  // this lane's 8 k
+#pragma unroll
+    for (int t = 0; t < 4 * G; ++t)
+      bload16_lds(rx, xw + t * XS + c * 64,
+                  off_if(ks < static_cast<uint32_t>(p.K) && t < p.M, static_cast<uint32_t>(t) * ldx_bytes + ks * 2));
+  }
+  uint32_t sw[C][NQ];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      sw[c][q] = bload4(rs, off_if(kv[c] && rv[q], static_cast<uint32_t>(scale_word_offset(row[q], k0[c] / 64, p.tiles))));
+  u32x4 wv[C][NQ];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      wv[c][q] = bload16_nt(rw, off_if(kv[c] && rv[q], static_cast<uint32_t>(row[q]) * row_bytes + k0[c] / 2));
+  __builtin_amdgcn_sched_barrier(0);
+
+  vm_wait<C * NQ * 2>();  // the activation loads (issued first) are in LDS
+  u32x4 xv[C][G][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) xv[c][g][h] = xw[(4 * g + jr) * XS + c * 64 + 4 * blk + h];
+  __builtin_amdgcn_sched_barrier(0);  // the LDS reads go out before the wait for the codes
+
+  const uint32_t shift = 16u * (blk & 1);  // scale bytes 2(b%2), 2(b%2)+1 of the word
+  f32x4 acc[NQ][G];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[q][g] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      u32x2 wb[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = wv[c][q][d];
+        wb[2 * d] = u32x2{e2m1x2_bf16<0>(w), e2m1x2_bf16<1>(w)};
+        wb[2 * d + 1] = u32x2{e2m1x2_bf16<2>(w), e2m1x2_bf16<3>(w)};
+      }
+      const float s0 = e4m3_to_f32<0>(sw[c][q] >> shift);
+      const float s1 = e4m3_to_f32<1>(sw[c][q] >> shift);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        f32x4 h0 = f32x4{0, 0, 0, 0}, h1 = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const u32x4& xa = xv[c][g][st / 2];
+          h0 = mfma_4x4x4(st % 2 ? u32x2{xa.z, xa.w} : u32x2{xa.x, xa.y}, wb[st], h0);
+        }
+#pragma unroll
+        for (int st = 4; st < 8; ++st) {
+          const u32x4& xa = xv[c][g][st / 2];
+          h1 = mfma_4x4x4(st % 2 ? u32x2{xa.z, xa.w} : u32x2{xa.x, xa.y}, wb[st], h1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[q][g][i] = __builtin_fmaf(h0[i], s0, acc[q][g][i]);
+          acc[q][g][i] = __builtin_fmaf(h1[i], s1, acc[q][g][i]);
+        }
+      }
+    }
+  }
+
+  // Sum the 16 blocks: two half-wave swaps halve the values per lane, then
+  // lanes 4 and 8 apart within each row of 16 are added (the lanes of one
+  // quad row stay apart).
+  float v[V];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[(q * G + g) * 4 + i] = acc[q][g][i];
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                    __builtin_bit_cast(uint32_t, v[j + V / 2]), false, false);
+    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                    __builtin_bit_cast(uint32_t, v[j + V / 4]), false, false);
+    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    v[j] += dpp_f32<0x124>(v[j]);  // row_ror:4
+    v[j] += dpp_f32<0x128>(v[j]);  // row_ror:8
+  }
+  if constexpr (KS > 1) {
+    __shared__ float red[4][V / 4][64];
+    if (kw > 0) {
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j) red[wave][j][lane] = v[j];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int s2 = 1; s2 < KS; ++s2)
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) v[j] += red[wave + s2][j][lane];
+    }
+  }
+  // lane l now holds values base + 0 .. V/4 - 1 of its quad row l % 4
+  const int base = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4);
+  if (kw == 0 && (lane & 12) == 0) {
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const int vi = base + j;
+      const int q = vi / (4 * G), m = vi % (4 * G);
+      // the row is selected, not indexed: a lane-dependent index into row[]
+      // would move the array to scratch
+      int64_t r = row[0];
+      bool ok = rv[0];
+#pragma unroll
+      for (int q2 = 1; q2 < NQ; ++q2)
+        if (q == q2) {
+          r = row[q2];
+          ok = rv[q2];
+        }
+      if (ok && m < p.M) p.out[m * static_cast<int64_t>(p.N) + r] = f32_to_bf16_bits(v[j] * gs);
     }
   }
 }
@@ -1014,6 +1219,11 @@ hipError_t launch_vchunk_c(GemvParams p, hipStream_t stream) {
 // and from M = 3 it is the faster one.
 constexpr int64_t kValuMaxMFp4 = 2;
 
+// The 4x4 block MFMA kernel: rows of up to two 512-k segments per lane and
+// 4 waves (K <= 4096), up to 8 tokens (two groups of 4).
+constexpr int64_t kBlkMaxK = 4096;
+constexpr int64_t kBlkMaxM = 8;
+
 // NVFP4 rows of at most kVchunkMaxK columns: 8-k chunks, at most 8 per lane
 // and 4 waves per unit.
 constexpr int64_t kVchunkMaxK = 64 * 8 * 8 * 4;
@@ -1158,9 +1368,63 @@ hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
+template <int G, int NQ, int C>
+hipError_t launch_blk_c(GemvParams p, hipStream_t stream) {
+  constexpr int KS = 4;
+  p.units = (p.units + NQ - 1) / NQ;
+  if (t_describe) {
+    std::snprintf(t_describe, t_describe_len, "k_gemv_blk<%d, %d, %d, %d>", G, NQ, C, KS);
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((k_gemv_blk<G, NQ, C, KS>), dim3(static_cast<unsigned>(p.units)), dim3(64 * KS), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int G, int NQ>
+hipError_t launch_blk_nq(const GemvParams& p, hipStream_t stream) {
+  if ((p.K + 511) / 512 <= 4) return launch_blk_c<G, NQ, 1>(p, stream);
+  return launch_blk_c<G, NQ, 2>(p, stream);
+}
+
+// Quads per unit: the fewest quads per compute unit on the busiest unit,
+// then the larger unit (its scale lines and activation reads serve more
+// rows).  Measured at 2..4 tokens: 4096 rows (1024 quads) 4 per unit, 6144
+// rows 3 (2 or 4 were 0.1-0.2 us slower, 6 and 8 slower still).
+int blk_quads_per_unit(int64_t quads) {
+  const int64_t cus = device_cu_count();
+  int best = 4;
+  int64_t best_load = (quads + 4 * cus - 1) / (4 * cus) * 4;
+  for (int nq = 3; nq >= 1; --nq) {
+    const int64_t load = (quads + nq * cus - 1) / (nq * cus) * nq;
+    if (load < best_load) {
+      best = nq;
+      best_load = load;
+    }
+  }
+  return best;
+}
+
+template <int G>
+hipError_t launch_blk(const GemvParams& p, hipStream_t stream) {
+  switch (blk_quads_per_unit(p.units)) {
+    case 1: return launch_blk_nq<G, 1>(p, stream);
+    case 2: return launch_blk_nq<G, 2>(p, stream);
+    case 3: return launch_blk_nq<G, 3>(p, stream);
+    default: return launch_blk_nq<G, 4>(p, stream);
+  }
+}
+
 template <bool FP4, bool SILU>
 hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
+  if constexpr (FP4 && !SILU) {
+    if (path == kPathBlk) {
+      p.tiles = p.K / 64;
+      p.units = ((limit + 127) / 128) * 32;
+      if (p.M <= 4) return launch_blk<1>(p, stream);
+      return launch_blk<2>(p, stream);  // (forced only)
+    }
+  }
   if (path == kPathValu) {
     p.tiles = FP4 ? p.K / 64 : p.K / 16;
     p.units = FP4 ? ((limit + 127) / 128) * 32 : (limit + 3) / 4;
@@ -1220,7 +1484,8 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
     //    2 splits over units of about 2 * tiles / (compute units) tiles.
     //    E.g. 4096 x 14336 NVFP4 at 32 tokens 21.4 -> 17.4 us, BF16 36.5 ->
     //    31.6 us; the 4096 x 4096 and 6144 x 4096 sweep shapes never split.
-    if (fp4 && M <= kValuMaxMFp4) return none;  // the VALU kernels take these
+    // the VALU and 4x4 block kernels take these
+    if (fp4 && (M <= kValuMaxMFp4 || default_gemv_path(fp4, M, N, K, silu) == kPathBlk)) return none;
     const int64_t cus = device_cu_count();
     const double w_tile = 16.0 * (silu ? 2 : 1) * static_cast<double>(K) * (fp4 ? 0.5625 : 2.0);
     const double a_wg = static_cast<double>(xt) * static_cast<double>(K) * 2.0;
@@ -1248,23 +1513,42 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   return SplitPlan{rt, s, kSplitCounterBytes, kSplitCounterBytes + units * s * na * nt * 64 * 16};
 }
 
-// VALU dot path for the smallest M and the MFMA path above it.  NVFP4 rows
-// of up to kVchunkMaxK columns take the chunked VALU kernel (M <= 4); other
-// VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
-// W4A16_GEMV_PATH=valu|mfma forces a path where it applies (the tests use it
-// to cover both at every M).
-int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K) {
+// NVFP4 without silu_mul: the VALU kernel at one token, the 4x4 block MFMA
+// kernel from 2 to 4 tokens (rows of up to kBlkMaxK columns), the 16x16
+// MFMA kernels above.  NVFP4 rows of up to kVchunkMaxK columns take the
+// chunked VALU kernel (M <= 2 by default, M <= 4 forced); other VALU cases
+// stage M <= 2 activation rows in a 64 KB LDS area.
+// W4A16_GEMV_PATH=valu|mfma|blk forces a path where it applies (the tests
+// use it to cover every family at every M).
+namespace {
+
+bool valu_fits(bool fp4, int64_t M, int64_t K) {
+  return (fp4 && K <= kVchunkMaxK) ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
+}
+bool blk_fits(bool fp4, int64_t M, int64_t K, int silu) { return fp4 && !silu && K <= kBlkMaxK && M <= kBlkMaxM; }
+
+}  // namespace
+
+int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   (void)N;
-  const bool chunked = fp4 && K <= kVchunkMaxK;
-  const bool valu_fits = chunked ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
-  if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
-    if (std::strcmp(env, "mfma") == 0) return kPathMfma;
-    if (std::strcmp(env, "valu") == 0 && valu_fits) return kPathValu;
-  }
+  // measured (µs, 4096 x 4096 / 6144 x 4096): 2 tokens 4.62 / 5.35 (VALU)
+  // -> 4.31 / 5.36, 4 tokens 4.86 / 6.51 (16x16 MFMA) -> 4.42 / 5.58; at
+  // 5..8 tokens the 16x16 MFMA kernels stay ahead (4x4x4 MFMAs are a
+  // quarter of their rate per product)
+  if (blk_fits(fp4, M, K, silu) && M >= 2 && M <= 4) return kPathBlk;
   // BF16 at M = 1: the MFMA path up to K = 8192 (measured 5% faster at
   // 4096), the VALU path beyond (2% faster at 14336)
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : (K <= 8192 ? 0 : 1);
-  return (valu_fits && M <= valu_max_m) ? kPathValu : kPathMfma;
+  return (valu_fits(fp4, M, K) && M <= valu_max_m) ? kPathValu : kPathMfma;
+}
+
+int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
+  if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
+    if (std::strcmp(env, "mfma") == 0) return kPathMfma;
+    if (std::strcmp(env, "valu") == 0 && valu_fits(fp4, M, K)) return kPathValu;
+    if (std::strcmp(env, "blk") == 0 && blk_fits(fp4, M, K, silu)) return kPathBlk;
+  }
+  return default_gemv_path(fp4, M, N, K, silu);
 }
 
 void describe_gemv(bool fp4, const GemvParams& p, int silu, int path, char* name, size_t len) {

@@ -9,6 +9,7 @@ namespace w4a16 {
 
 constexpr int kPathValu = 0;
 constexpr int kPathMfma = 1;
+constexpr int kPathBlk = 2;
 
 struct GemvParams {
   const uint16_t* x;   // bf16 [M][ldx]
@@ -50,7 +51,10 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
 constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
-int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K);
+// The kernel family a GEMV call uses: the measured default, or the one that
+// W4A16_GEMV_PATH forces where it applies.
+int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
+int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu);
 hipError_t launch_gemv(bool fp4, const GemvParams& p, int silu, int path, hipStream_t stream);
 // Runs the GEMV dispatch without launching: writes the name of the kernel
 // instantiation launch_gemv would launch for these sizes into name.
