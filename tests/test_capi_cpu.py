@@ -186,17 +186,20 @@ def test_gemv_kernel_name_query(monkeypatch):
     from w4a16_nvfp4_gemv_amd import W4A16Error, gemv_kernel_name
     monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_vchunk<1, false,")
-    for m in (1, 2):
-        assert gemv_kernel_name(m, 28672, 4096, silu_mul=True).startswith(f"k_gemv_vchunk<{m}, true,")
+    assert gemv_kernel_name(1, 28672, 4096, silu_mul=True).startswith("k_gemv_vchunk<1, true,")
+    assert gemv_kernel_name(2, 4096, 8192).startswith("k_gemv_vchunk<2, false,")  # K > 4096
     # 2..4 tokens without silu_mul: the 4x4 block MFMA kernel, with the quads per
     # unit that balance the compute units (the host-only query assumes 256 compute
     # units when no GPU is present) and one or two 512-k segments per lane
     for m in (2, 3, 4):
-        assert gemv_kernel_name(m, 4096, 4096) == "k_gemv_blk<1, 4, 2, 4>"
-        assert gemv_kernel_name(m, 6144, 4096) == "k_gemv_blk<1, 3, 2, 4>"
-    assert gemv_kernel_name(2, 2048, 4096) == "k_gemv_blk<1, 2, 2, 4>"
-    assert gemv_kernel_name(3, 1024, 2048) == "k_gemv_blk<1, 1, 1, 4>"
+        assert gemv_kernel_name(m, 4096, 4096) == "k_gemv_blk<1, 4, 2, 4, false>"
+        assert gemv_kernel_name(m, 6144, 4096) == "k_gemv_blk<1, 3, 2, 4, false>"
+    assert gemv_kernel_name(2, 2048, 4096) == "k_gemv_blk<1, 2, 2, 4, false>"
+    assert gemv_kernel_name(3, 1024, 2048) == "k_gemv_blk<1, 1, 1, 4, false>"
     assert gemv_kernel_name(4, 4096, 8192).startswith("k_gemv_mfma<true, 4, false,")  # K > 4096
+    for m in (2, 4):  # with silu_mul: units of 4 or 3 gate quads and their up quads
+        assert gemv_kernel_name(m, 28672, 4096, silu_mul=True) == "k_gemv_blk<1, 4, 2, 4, true>"
+        assert gemv_kernel_name(m, 2 * 6144, 4096, silu_mul=True) == "k_gemv_blk<1, 3, 2, 4, true>"
     # the MFMA kernels are named by the token rows they stage per step
     for m, xt in ((5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
@@ -205,11 +208,10 @@ def test_gemv_kernel_name_query(monkeypatch):
     # 5..8 tokens where 24-row units fit the compute units and 16-row tiles do not
     for m in (5, 8):
         assert gemv_kernel_name(m, 6144, 4096) == "k_gemv_mfma_bd<false, 8, 24>"
-    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 4, 24>"
     assert gemv_kernel_name(8, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 24>"
     # 5..8 tokens where only 56-row units fit (the fused silu call on 2 x 14336 rows)
     assert gemv_kernel_name(8, 28672, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 56>"
-    assert gemv_kernel_name(4, 28672, 4096, silu_mul=True).startswith("k_gemv_mfma<true, 4, true,")
+    assert gemv_kernel_name(4, 28672, 8192, silu_mul=True).startswith("k_gemv_mfma<true, 4, true,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
     # BF16 at one token: MFMA up to K = 8192, the VALU kernel beyond
@@ -219,11 +221,13 @@ def test_gemv_kernel_name_query(monkeypatch):
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     for m, tk in ((3, 4), (4, 4)):
         assert gemv_kernel_name(m, 6144, 4096) == f"k_gemv_mfma_bd<false, {tk}, 24>"
+    assert gemv_kernel_name(4, 2 * 6144, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 4, 24>"
     monkeypatch.setenv("W4A16_GEMV_PATH", "blk")
-    assert gemv_kernel_name(1, 4096, 4096) == "k_gemv_blk<1, 4, 2, 4>"
-    assert gemv_kernel_name(8, 4096, 4096) == "k_gemv_blk<2, 4, 2, 4>"
+    assert gemv_kernel_name(1, 4096, 4096) == "k_gemv_blk<1, 4, 2, 4, false>"
+    assert gemv_kernel_name(8, 4096, 4096) == "k_gemv_blk<2, 4, 2, 4, false>"
     assert gemv_kernel_name(9, 4096, 4096).startswith("k_gemv_mfma<true, 16, false,")  # beyond 8 tokens
-    assert gemv_kernel_name(2, 28672, 4096, silu_mul=True).startswith("k_gemv_vchunk<2, true,")
+    assert gemv_kernel_name(2, 28672, 4096, silu_mul=True) == "k_gemv_blk<1, 4, 2, 4, true>"
+    assert gemv_kernel_name(8, 28672, 4096, silu_mul=True) == "k_gemv_blk<2, 4, 2, 4, true>"
     monkeypatch.setenv("W4A16_GEMV_PATH", "valu")
     assert gemv_kernel_name(4, 4096, 4096).startswith("k_gemv_vchunk<4, false,")
     assert gemv_kernel_name(64, 6144, 4096).endswith(", 2, 1>")  # two row tiles per workgroup
@@ -266,7 +270,7 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
         assert gemv_kernel_name(m, 1024, 8192, splitk=True) == f"k_gemv_mfma<true, {xt}, false, 1, 4>"
         assert lib.gemv_splitk_workspace_bytes(1, m, 1024, 8192, 0) == 65536 + 64 * 4 * nt * 1024
     assert gemv_kernel_name(8, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 8, false, 1, 1>"  # too little work
-    assert gemv_kernel_name(4, 1024, 4096, splitk=True) == "k_gemv_blk<1, 1, 2, 4>"  # the 4x4 kernel: no split
+    assert gemv_kernel_name(4, 1024, 4096, splitk=True) == "k_gemv_blk<1, 1, 2, 4, false>"  # the 4x4 kernel: no split
     assert gemv_kernel_name(32, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 32, false, 1, 2>"
     assert gemv_kernel_name(32, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 32, false, 2, 2>"
     assert lib.gemv_splitk_workspace_bytes(1, 32, 4096, 14336, 0) == 65536 + 128 * 2 * 2 * 2 * 1024

@@ -131,12 +131,28 @@ def test_nvfp4_gemv_4x4_block_kernel(m, n, nq, k, c, monkeypatch):
     512-k segments per lane, ragged K (waves and lanes past the end of a row),
     a partial band (48 rows), every output checked."""
     monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
-    assert lib.gemv_kernel_name(m, n, k) == f"k_gemv_blk<1, {nq}, {c}, 4>"
+    assert lib.gemv_kernel_name(m, n, k) == f"k_gemv_blk<1, {nq}, {c}, 4, false>"
     _say("nvfp4_gemv blk", m, n, k)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 3 * n + k)
     got = run_nvfp4(d, n)
     _, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n)
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv blk M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [2, 3, 4])
+@pytest.mark.parametrize("n,nq", [(96, 1), (2 * 2048, 2), (2 * 6144, 3), (2 * 14336, 4)])
+@pytest.mark.parametrize("k,c", [(64, 1), (2560, 2), (4096, 2)])
+def test_nvfp4_gemv_4x4_block_kernel_silu(m, n, nq, k, c, monkeypatch):
+    """The 4x4 block MFMA kernel with silu_mul: units of nq gate quads and
+    their up quads (the up rows n/2 further on, in another band), every
+    output checked."""
+    monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
+    assert lib.gemv_kernel_name(m, n, k, silu_mul=True) == f"k_gemv_blk<1, {nq}, {c}, 4, true>"
+    _say("nvfp4_gemv blk silu", m, n, k)
+    d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(2, m) + 5 * n + k)
+    got = run_nvfp4(d, n, silu=True)
+    want, acc, absacc = oracle.nvfp4_gemv(d["x"], d["w"], d["s"], float(d["gs"][0]), n, silu_mul=True)
+    check_silu(got, want, acc, absacc, d["gs"][0], f"silu blk M={m} N={n} K={k}")
 
 
 @pytest.mark.parametrize("m", [33, 47, 64])

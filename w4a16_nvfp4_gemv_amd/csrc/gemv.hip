@@ -1,16 +1,17 @@
 // Dense small-M GEMV kernels for gfx950: out = bf16(fp32(x @ W^T) * gs).
 //
 // Four kernel families serve the same entry points:
-//   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns and M <= 2 tokens
-//     (one token without silu_mul; up to 4 when the VALU path is forced).
+//   * k_gemv_vchunk -- NVFP4 rows of up to 16384 columns at one token (two
+//     for rows longer than 4096; up to 4 when the VALU path is forced).
 //     VALU dot products over exactly decoded BF16 pairs (v_dot2_f32_bf16);
 //     lanes own interleaved 8-k chunks so that every load instruction of a
 //     wave reads one contiguous stretch, and a permlane reduce-scatter sums
 //     the lanes.
-//   * k_gemv_blk -- NVFP4 without silu_mul, 2..4 tokens, rows of up to 4096
-//     columns: the same streaming as k_gemv_vchunk (256 contiguous bytes of a
-//     row per load, every load issued up front), with the products on
-//     v_mfma_f32_4x4x4_16b_bf16, whose 16 blocks take 16 k ranges of 4 rows.
+//   * k_gemv_blk -- NVFP4 at 2..4 tokens, rows of up to 4096 columns (with
+//     or without silu_mul): the same streaming as k_gemv_vchunk (256
+//     contiguous bytes of a row per load, every load issued up front), with
+//     the products on v_mfma_f32_4x4x4_16b_bf16, whose 16 blocks take 16 k
+//     ranges of 4 rows.
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
 //     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 beyond
 //     8192 columns and NVFP4 rows longer than 16384 columns at M <= 2.
@@ -470,9 +471,11 @@ __device__ __forceinline__ f32x4 mfma_4x4x4(u32x2 a, u32x2 b, const f32x4& c) {
                                                 0);
 }
 
-template <int G, int NQ, int C, int KS>
+template <int G, int NQ, int C, int KS, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
-  constexpr int V = NQ * G * 4;  // values per lane: v = (q * G + g) * 4 + i
+  constexpr int NA = SILU ? 2 * NQ : NQ;  // quads per unit: NQ (gate) quads, then their up quads
+  constexpr int P = SILU ? 2 : 1;
+  constexpr int V = NQ * G * 4 * P;  // values per lane: v = ((q * G + g) * 4 + i) * P + u
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -480,6 +483,7 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
   const int64_t unit = static_cast<int64_t>(xcd_logical_block()) * (4 / KS) + wave / KS;
   const int jr = lane & 3;   // row of the quad (B column) / token of the group (A row)
   const int blk = lane >> 2;  // k range
+  const int64_t limit = SILU ? p.half : p.N;
   const uint32_t row_bytes = p.K / 2;
   const uint32_t ldx_bytes = static_cast<uint32_t>(p.ldx) * 2;
   const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
@@ -488,13 +492,17 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
   const float gs = *p.gs;
 
   // this lane's row in each quad of the unit
-  int64_t row[NQ];
-  bool rv[NQ];
+  int64_t row[NA];
+  bool rv[NA];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int64_t qi = unit * NQ + q;
     row[q] = (qi >> 5) * 128 + (qi & 31) + 32 * jr;
-    rv[q] = row[q] < p.N && unit < p.units;
+    rv[q] = row[q] < limit && unit < p.units;
+    if constexpr (SILU) {
+      row[NQ + q] = row[q] + p.half;
+      rv[NQ + q] = rv[q];
+    }
   }
   uint32_t k0[C];
   bool kv[C];
@@ -518,21 +526,21 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
       bload16_lds(rx, xw + t * XS + c * 64,
                   off_if(ks < static_cast<uint32_t>(p.K) && t < p.M, static_cast<uint32_t>(t) * ldx_bytes + ks * 2));
   }
-  uint32_t sw[C][NQ];
+  uint32_t sw[C][NA];
 #pragma unroll
   for (int c = 0; c < C; ++c)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      sw[c][q] = bload4(rs, off_if(kv[c] && rv[q], static_cast<uint32_t>(scale_word_offset(row[q], k0[c] / 64, p.tiles))));
-  u32x4 wv[C][NQ];
+    for (int a = 0; a < NA; ++a)
+      sw[c][a] = bload4(rs, off_if(kv[c] && rv[a], static_cast<uint32_t>(scale_word_offset(row[a], k0[c] / 64, p.tiles))));
+  u32x4 wv[C][NA];
 #pragma unroll
   for (int c = 0; c < C; ++c)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      wv[c][q] = bload16_nt(rw, off_if(kv[c] && rv[q], static_cast<uint32_t>(row[q]) * row_bytes + k0[c] / 2));
+    for (int a = 0; a < NA; ++a)
+      wv[c][a] = bload16_nt(rw, off_if(kv[c] && rv[a], static_cast<uint32_t>(row[a]) * row_bytes + k0[c] / 2));
   __builtin_amdgcn_sched_barrier(0);
 
-  vm_wait<C * NQ * 2>();  // the activation loads (issued first) are in LDS
+  vm_wait<C * NA * 2>();  // the activation loads (issued first) are in LDS
   u32x4 xv[C][G][4];
 #pragma unroll
   for (int c = 0; c < C; ++c)
@@ -543,24 +551,24 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
   __builtin_amdgcn_sched_barrier(0);  // the LDS reads go out before the wait for the codes
 
   const uint32_t shift = 16u * (blk & 1);  // scale bytes 2(b%2), 2(b%2)+1 of the word
-  f32x4 acc[NQ][G];
+  f32x4 acc[NA][G];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[q][g] = f32x4{0, 0, 0, 0};
+    for (int g = 0; g < G; ++g) acc[a][g] = f32x4{0, 0, 0, 0};
 #pragma unroll
   for (int c = 0; c < C; ++c) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int a = 0; a < NA; ++a) {
       u32x2 wb[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wv[c][q][d];
+        const uint32_t w = wv[c][a][d];
         wb[2 * d] = u32x2{e2m1x2_bf16<0>(w), e2m1x2_bf16<1>(w)};
         wb[2 * d + 1] = u32x2{e2m1x2_bf16<2>(w), e2m1x2_bf16<3>(w)};
       }
-      const float s0 = e4m3_to_f32<0>(sw[c][q] >> shift);
-      const float s1 = e4m3_to_f32<1>(sw[c][q] >> shift);
+      const float s0 = e4m3_to_f32<0>(sw[c][a] >> shift);
+      const float s1 = e4m3_to_f32<1>(sw[c][a] >> shift);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         f32x4 h0 = f32x4{0, 0, 0, 0}, h1 = f32x4{0, 0, 0, 0};
@@ -576,8 +584,8 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[q][g][i] = __builtin_fmaf(h0[i], s0, acc[q][g][i]);
-          acc[q][g][i] = __builtin_fmaf(h1[i], s1, acc[q][g][i]);
+          acc[a][g][i] = __builtin_fmaf(h0[i], s0, acc[a][g][i]);
+          acc[a][g][i] = __builtin_fmaf(h1[i], s1, acc[a][g][i]);
         }
       }
     }
@@ -585,14 +593,17 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
 
   // Sum the 16 blocks: two half-wave swaps halve the values per lane, then
   // lanes 4 and 8 apart within each row of 16 are added (the lanes of one
-  // quad row stay apart).
+  // quad row stay apart).  V / 4 is even with silu_mul, so a gate value and
+  // its up value stay in one lane.
   float v[V];
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[(q * G + g) * 4 + i] = acc[q][g][i];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < P; ++u) v[((q * G + g) * 4 + i) * P + u] = acc[u * NQ + q][g][i];
 #pragma unroll
   for (int j = 0; j < V / 2; ++j) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
@@ -628,9 +639,9 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
   const int base = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4);
   if (kw == 0 && (lane & 12) == 0) {
 #pragma unroll
-    for (int j = 0; j < V / 4; ++j) {
-      const int vi = base + j;
-      const int q = vi / (4 * G), m = vi % (4 * G);
+    for (int j = 0; j < V / 4 / P; ++j) {
+      const int t = (base + j * P) / P;
+      const int q = t / (4 * G), m = t % (4 * G);
       // the row is selected, not indexed: a lane-dependent index into row[]
       // would move the array to scratch
       int64_t r = row[0];
@@ -641,7 +652,14 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
           r = row[q2];
           ok = rv[q2];
         }
-      if (ok && m < p.M) p.out[m * static_cast<int64_t>(p.N) + r] = f32_to_bf16_bits(v[j] * gs);
+      if (!ok || m >= p.M) continue;
+      if constexpr (!SILU) {
+        p.out[m * static_cast<int64_t>(p.N) + r] = f32_to_bf16_bits(v[j] * gs);
+      } else {
+        const float gv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P] * gs));
+        const float uv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P + 1] * gs));
+        p.out[m * static_cast<int64_t>(p.half) + r] = f32_to_bf16_bits(silu_f32(gv) * uv);
+      }
     }
   }
 }
@@ -1368,61 +1386,65 @@ hipError_t launch_mfma(GemvParams p, hipStream_t stream) {
   return launch_mfma_rt<FP4, XT, SILU, 1>(p, stream);
 }
 
-template <int G, int NQ, int C>
+template <int G, int NQ, int C, bool SILU>
 hipError_t launch_blk_c(GemvParams p, hipStream_t stream) {
   constexpr int KS = 4;
   p.units = (p.units + NQ - 1) / NQ;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_blk<%d, %d, %d, %d>", G, NQ, C, KS);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_blk<%d, %d, %d, %d, %s>", G, NQ, C, KS, tf(SILU));
     return hipSuccess;
   }
-  hipLaunchKernelGGL((k_gemv_blk<G, NQ, C, KS>), dim3(static_cast<unsigned>(p.units)), dim3(64 * KS), 0, stream, p);
+  hipLaunchKernelGGL((k_gemv_blk<G, NQ, C, KS, SILU>), dim3(static_cast<unsigned>(p.units)), dim3(64 * KS), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-template <int G, int NQ>
+template <int G, int NQ, bool SILU>
 hipError_t launch_blk_nq(const GemvParams& p, hipStream_t stream) {
-  if ((p.K + 511) / 512 <= 4) return launch_blk_c<G, NQ, 1>(p, stream);
-  return launch_blk_c<G, NQ, 2>(p, stream);
+  if ((p.K + 511) / 512 <= 4) return launch_blk_c<G, NQ, 1, SILU>(p, stream);
+  return launch_blk_c<G, NQ, 2, SILU>(p, stream);
 }
 
-// Quads per unit: the fewest quads per compute unit on the busiest unit,
-// then the larger unit (its scale lines and activation reads serve more
-// rows).  Measured at 2..4 tokens: 4096 rows (1024 quads) 4 per unit, 6144
-// rows 3 (2 or 4 were 0.1-0.2 us slower, 6 and 8 slower still).
+// Quads per unit: the busiest compute unit's rounds of units times the
+// quads of a unit plus one (a unit's fixed cost, its activation reads and
+// reduction, counted as one quad); ties go to the larger unit.  Measured at
+// 2..4 tokens: 4096 rows (1024 quads) 4 per unit, 6144 rows 3 (2 or 4 were
+// 0.1-0.2 us slower, 6 and 8 slower still), the fused silu call on 2 x 14336
+// rows 4 (0.05-0.2 us ahead of 2, 1 was 1.8-3.7 us slower).
 int blk_quads_per_unit(int64_t quads) {
   const int64_t cus = device_cu_count();
-  int best = 4;
-  int64_t best_load = (quads + 4 * cus - 1) / (4 * cus) * 4;
-  for (int nq = 3; nq >= 1; --nq) {
-    const int64_t load = (quads + nq * cus - 1) / (nq * cus) * nq;
-    if (load < best_load) {
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int nq = 4; nq >= 1; --nq) {
+    const int64_t units = (quads + nq - 1) / nq;
+    const int64_t cost = (units + cus - 1) / cus * (nq + 1);
+    if (best == 0 || cost < best_cost) {
       best = nq;
-      best_load = load;
+      best_cost = cost;
     }
   }
   return best;
 }
 
-template <int G>
+template <int G, bool SILU>
 hipError_t launch_blk(const GemvParams& p, hipStream_t stream) {
   switch (blk_quads_per_unit(p.units)) {
-    case 1: return launch_blk_nq<G, 1>(p, stream);
-    case 2: return launch_blk_nq<G, 2>(p, stream);
-    case 3: return launch_blk_nq<G, 3>(p, stream);
-    default: return launch_blk_nq<G, 4>(p, stream);
+    case 1: return launch_blk_nq<G, 1, SILU>(p, stream);
+    case 2: return launch_blk_nq<G, 2, SILU>(p, stream);
+    case 3: return launch_blk_nq<G, 3, SILU>(p, stream);
+    default: return launch_blk_nq<G, 4, SILU>(p, stream);
   }
 }
 
 template <bool FP4, bool SILU>
 hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
-  if constexpr (FP4 && !SILU) {
+  if constexpr (FP4) {
     if (path == kPathBlk) {
       p.tiles = p.K / 64;
       p.units = ((limit + 127) / 128) * 32;
-      if (p.M <= 4) return launch_blk<1>(p, stream);
-      return launch_blk<2>(p, stream);  // (forced only)
+      if (p.M <= 4) return launch_blk<1, SILU>(p, stream);
+      return launch_blk<2, SILU>(p, stream);
     }
   }
   if (path == kPathValu) {
@@ -1513,11 +1535,11 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   return SplitPlan{rt, s, kSplitCounterBytes, kSplitCounterBytes + units * s * na * nt * 64 * 16};
 }
 
-// NVFP4 without silu_mul: the VALU kernel at one token, the 4x4 block MFMA
-// kernel from 2 to 4 tokens (rows of up to kBlkMaxK columns), the 16x16
-// MFMA kernels above.  NVFP4 rows of up to kVchunkMaxK columns take the
-// chunked VALU kernel (M <= 2 by default, M <= 4 forced); other VALU cases
-// stage M <= 2 activation rows in a 64 KB LDS area.
+// NVFP4: the VALU kernel at one token (and at two for rows longer than
+// kBlkMaxK columns), the 4x4 block MFMA kernel from 2 to 4 tokens (rows of
+// up to kBlkMaxK columns), the 16x16 MFMA kernels above.  NVFP4 rows of up
+// to kVchunkMaxK columns take the chunked VALU kernel (M <= 4 when forced);
+// other VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
 // W4A16_GEMV_PATH=valu|mfma|blk forces a path where it applies (the tests
 // use it to cover every family at every M).
 namespace {
@@ -1525,17 +1547,19 @@ namespace {
 bool valu_fits(bool fp4, int64_t M, int64_t K) {
   return (fp4 && K <= kVchunkMaxK) ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
 }
-bool blk_fits(bool fp4, int64_t M, int64_t K, int silu) { return fp4 && !silu && K <= kBlkMaxK && M <= kBlkMaxM; }
+bool blk_fits(bool fp4, int64_t M, int64_t K) { return fp4 && K <= kBlkMaxK && M <= kBlkMaxM; }
 
 }  // namespace
 
 int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   (void)N;
-  // measured (µs, 4096 x 4096 / 6144 x 4096): 2 tokens 4.62 / 5.35 (VALU)
-  // -> 4.31 / 5.36, 4 tokens 4.86 / 6.51 (16x16 MFMA) -> 4.42 / 5.58; at
+  // measured (µs, 4096 x 4096 / 6144 x 4096 / the fused silu call on
+  // 2 x 14336 rows): 2 tokens 4.62 / 5.35 / 16.1 (VALU) -> 4.31 / 5.36 /
+  // 14.4, 4 tokens 4.86 / 6.51 / 19.9 (16x16 MFMA) -> 4.42 / 5.58 / 14.9; at
   // 5..8 tokens the 16x16 MFMA kernels stay ahead (4x4x4 MFMAs are a
-  // quarter of their rate per product)
-  if (blk_fits(fp4, M, K, silu) && M >= 2 && M <= 4) return kPathBlk;
+  // quarter of their rate per product, and 8 tokens' activations halve the
+  // workgroups per compute unit)
+  if (blk_fits(fp4, M, K) && M >= 2 && M <= 4) return kPathBlk;
   // BF16 at M = 1: the MFMA path up to K = 8192 (measured 5% faster at
   // 4096), the VALU path beyond (2% faster at 14336)
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : (K <= 8192 ? 0 : 1);
@@ -1546,7 +1570,7 @@ int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
     if (std::strcmp(env, "mfma") == 0) return kPathMfma;
     if (std::strcmp(env, "valu") == 0 && valu_fits(fp4, M, K)) return kPathValu;
-    if (std::strcmp(env, "blk") == 0 && blk_fits(fp4, M, K, silu)) return kPathBlk;
+    if (std::strcmp(env, "blk") == 0 && blk_fits(fp4, M, K)) return kPathBlk;
   }
   return default_gemv_path(fp4, M, N, K, silu);
 }
