@@ -83,6 +83,8 @@ def source_digest(csrc: str | None = None) -> str:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             code = [line.split("//", 1)[0].rstrip() for line in fh]
         h.update(f.encode() + "\n".join(c for c in code if c).encode())
+    from w4a16_nvfp4_gemv_amd import build_ext
+    h.update(" ".join(build_ext.CODEGEN_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -52,11 +52,23 @@ def build_probe(verbose: bool = False) -> str:
     return PROBE_LIB
 
 
+# Code-generation flags of the library (also part of the benchmark's source
+# digest: counter figures taken on code built otherwise are stale).
+CODEGEN_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+    # packed FP32 instructions stay off (only scalar / non-packed FP32 code)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs rather than AccVGPRs: the kernels read them with
+    # ordinary VALU instructions (block scales, reductions, epilogues), and
+    # each AccVGPR read costs a v_accvgpr_read (measured: the fused silu call
+    # at 32 tokens 29.3 -> 28.4 us, the 4x4 block kernel 0.06-0.3 us faster)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
+]
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed FP32 instructions stay off (only scalar / non-packed FP32 code)
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        hipcc(), *CODEGEN_FLAGS, "-fPIC", "-shared",
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
         "-I", os.path.join(ROOT, "include"),
         *sources(), "-o", LIB + ".tmp",

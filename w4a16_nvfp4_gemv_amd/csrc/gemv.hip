@@ -526,6 +526,7 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
       bload16_lds(rx, xw + t * XS + c * 64,
                   off_if(ks < static_cast<uint32_t>(p.K) && t < p.M, static_cast<uint32_t>(t) * ldx_bytes + ks * 2));
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load below is issued after these (the wait counts them)
   uint32_t sw[C][NA];
 #pragma unroll
   for (int c = 0; c < C; ++c)
@@ -835,6 +836,10 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
         bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64,
                     off_if(sv && k < static_cast<uint32_t>(p.K), sxo[i] + k * 2));
       }
+      // The waits below count the loads issued after a slot's staging loads:
+      // the scheduler keeps each step's staging loads, then its weight loads,
+      // in the order written.
+      __builtin_amdgcn_sched_barrier(0);
       const uint32_t k = kb + (FP4 ? g * 32 : g * 8);
       const bool kv = sv && k < static_cast<uint32_t>(p.K);
 #pragma unroll
@@ -859,6 +864,7 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);
@@ -1088,6 +1094,8 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
         bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + q * 64,
                     off_if(sv && k < static_cast<uint32_t>(p.K), sxo[q] + k * 2));
       }
+      // staging loads, then weight loads, in the order the waits count them
+      __builtin_amdgcn_sched_barrier(0);
       // K % 64 == 0: the lane's 32 codes are all in range or all out
       const uint32_t k = kb + 128 * c + 32 * g;
       const bool kv = sv && k < static_cast<uint32_t>(p.K);
@@ -1097,6 +1105,7 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
         sb[d][a] = bload4(rs, ok ? static_cast<uint32_t>(scale_word_offset(rows[a], k / 64, p.tiles)) : kOutOfRange);
         wb[d][a] = bload16_nt(rw, ok ? static_cast<uint32_t>(rows[a]) * row_bytes + k / 2 : kOutOfRange);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d, d);

@@ -599,6 +599,8 @@ __global__ __launch_bounds__(kMoeGateUpWaves * 64) void k_moe_gate_up_mfma(const
       bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64,
                   off_if(valid && k < static_cast<uint32_t>(p.H), sxo[i] + k * 2));
     }
+    // staging loads, then weight loads, in the order the waits count them
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t k = kb + g * 32;
     const bool kv = valid && k < static_cast<uint32_t>(p.H);
 #pragma unroll
@@ -781,6 +783,8 @@ __global__ __launch_bounds__(kMoeDownWaves * 64) void k_moe_down_mfma(const MoeD
         const uint32_t k = kb + skc[i];
         bload16_lds(rx, xl_slot<W * SLOT>(d) + wave * SLOT + i * 64, off_if(valid && k < kdim, sxo[i] + k * 2));
       }
+      // staging loads, then weight loads, in the order the waits count them
+      __builtin_amdgcn_sched_barrier(0);
       const uint32_t k = kb + g * 32;
       const bool ok = valid && rvalid && k < kdim;
       sb[d] = bload4(rs, off_if(ok, static_cast<uint32_t>(scale_word_offset(row, k / 64, kdim / 64))));
