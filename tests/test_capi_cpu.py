@@ -212,11 +212,17 @@ def test_gemv_kernel_name_query(monkeypatch):
     # 5..8 tokens where only 56-row units fit (the fused silu call on 2 x 14336 rows)
     assert gemv_kernel_name(8, 28672, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 56>"
     assert gemv_kernel_name(4, 28672, 8192, silu_mul=True).startswith("k_gemv_mfma<true, 4, true,")
-    assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
-    # BF16 at one token: MFMA up to K = 8192, the VALU kernel beyond
-    assert gemv_kernel_name(1, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
-    assert gemv_kernel_name(1, 4096, 14336, weight_fp4=False).startswith("k_gemv_valu<false, 1,")
+    # BF16 at 1..4 tokens: the 4x4 block kernel up to K = 14336 (without silu_mul);
+    # at one token beyond that the VALU kernel
+    for m in (1, 4):
+        assert gemv_kernel_name(m, 4096, 4096, weight_fp4=False) == "k_gemv_blkh<4, 4, 4>"
+        assert gemv_kernel_name(m, 4096, 14336, weight_fp4=False) == "k_gemv_blkh<4, 4, 4>"
+    assert gemv_kernel_name(2, 1024, 14336, weight_fp4=False) == "k_gemv_blkh<1, 4, 4>"
+    assert gemv_kernel_name(5, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 8, false,")
+    assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False, silu_mul=True).startswith("k_gemv_mfma<false, 4, true,")
+    assert gemv_kernel_name(1, 4096, 16384, weight_fp4=False).startswith("k_gemv_valu<false, 1,")
+    assert gemv_kernel_name(4, 4096, 16384, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     for m, tk in ((3, 4), (4, 4)):

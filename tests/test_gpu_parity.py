@@ -544,6 +544,23 @@ def test_bf16_gemv_small_shapes(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("n,nq", [(48, 1), (2048, 2), (3072, 3), (4096, 4)])
+@pytest.mark.parametrize("k", [16, 1040, 1536, 2560, 14336])
+def test_bf16_gemv_4x4_block_kernel(m, n, nq, k, monkeypatch):
+    """The BF16 4x4 block kernel at 1..4 tokens: every unit size, a piece cut
+    by the end of the row (K % 128 != 0), waves without pieces (K = 16), a
+    last round of fewer pieces (K = 1536, 2560), the longest rows (two rounds
+    in flight, 7 activation loads per token), every output checked."""
+    monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
+    assert lib.gemv_kernel_name(m, n, k, weight_fp4=False) == f"k_gemv_blkh<{nq}, 4, 4>"
+    _say("bf16_gemv blkh", m, n, k)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 7 * n + k)
+    got = run_bf16(d)
+    _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"])
+    check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv blkh M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("m", [1, 4, 16, 32])
 @pytest.mark.parametrize("n,k,variant", [(4096, 4096, 0), (4096, 14336, 1)])
 def test_bf16_gemv_full_size(m, n, k, variant):

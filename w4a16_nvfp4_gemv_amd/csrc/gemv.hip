@@ -11,10 +11,11 @@
 //     or without silu_mul): the same streaming as k_gemv_vchunk (256
 //     contiguous bytes of a row per load, every load issued up front), with
 //     the products on v_mfma_f32_4x4x4_16b_bf16, whose 16 blocks take 16 k
-//     ranges of 4 rows.
+//     ranges of 4 rows.  k_gemv_blkh is its BF16-weight form (1..4 tokens,
+//     rows of up to 14336 columns, without silu_mul).
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
 //     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 beyond
-//     8192 columns and NVFP4 rows longer than 16384 columns at M <= 2.
+//     14336 columns and NVFP4 rows longer than 16384 columns at M <= 2.
 //   * k_gemv_mfma -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
 //     weight rows of a tile are the A operand, up to 16 tokens the B operand,
 //     staged through an LDS ring.  The waves of a workgroup split K and
@@ -471,11 +472,91 @@ __device__ __forceinline__ f32x4 mfma_4x4x4(u32x2 a, u32x2 b, const f32x4& c) {
                                                 0);
 }
 
+// The end of a 4x4 block kernel: acc[a][g] holds, in item i of lane 4b+j,
+// block b's partial sum for row j of quad a and token 4g+i.  Sums the 16
+// blocks (two half-wave swaps halve the values per lane, then lanes 4 and 8
+// apart within each row of 16 are added, so the lanes of one quad row stay
+// apart; V / 4 is even with silu_mul, so a gate value and its up value stay
+// in one lane), adds the KS waves of the unit in slice order through LDS and
+// stores the rows (row[q], the lane's row of quad q).
+template <int G, int NQ, int KS, bool SILU>
+__device__ __forceinline__ void blk_finish(const GemvParams& p, const f32x4 (&acc)[SILU ? 2 * NQ : NQ][G],
+                                           const int64_t (&row)[SILU ? 2 * NQ : NQ], const bool (&rv)[SILU ? 2 * NQ : NQ],
+                                           float gs, int lane, int wave, int kw) {
+  constexpr int P = SILU ? 2 : 1;
+  constexpr int V = NQ * G * 4 * P;  // values per lane: v = ((q * G + g) * 4 + i) * P + u
+  float v[V];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < P; ++u) v[((q * G + g) * 4 + i) * P + u] = acc[u * NQ + q][g][i];
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                    __builtin_bit_cast(uint32_t, v[j + V / 2]), false, false);
+    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                    __builtin_bit_cast(uint32_t, v[j + V / 4]), false, false);
+    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    v[j] += dpp_f32<0x124>(v[j]);  // row_ror:4
+    v[j] += dpp_f32<0x128>(v[j]);  // row_ror:8
+  }
+  if constexpr (KS > 1) {
+    __shared__ float red[4][V / 4][64];
+    if (kw > 0) {
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j) red[wave][j][lane] = v[j];
+    }
+    __syncthreads();
+    if (kw == 0) {
+#pragma unroll
+      for (int s2 = 1; s2 < KS; ++s2)
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) v[j] += red[wave + s2][j][lane];
+    }
+  }
+  // lane l now holds values base + 0 .. V/4 - 1 of its quad row l % 4
+  const int base = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4);
+  if (kw == 0 && (lane & 12) == 0) {
+#pragma unroll
+    for (int j = 0; j < V / 4 / P; ++j) {
+      const int t = (base + j * P) / P;
+      const int q = t / (4 * G), m = t % (4 * G);
+      // the row is selected, not indexed: a lane-dependent index into row[]
+      // would move the array to scratch
+      int64_t r = row[0];
+      bool ok = rv[0];
+#pragma unroll
+      for (int q2 = 1; q2 < NQ; ++q2)
+        if (q == q2) {
+          r = row[q2];
+          ok = rv[q2];
+        }
+      if (!ok || m >= p.M) continue;
+      if constexpr (!SILU) {
+        p.out[m * static_cast<int64_t>(p.N) + r] = f32_to_bf16_bits(v[j] * gs);
+      } else {
+        const float gv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P] * gs));
+        const float uv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P + 1] * gs));
+        p.out[m * static_cast<int64_t>(p.half) + r] = f32_to_bf16_bits(silu_f32(gv) * uv);
+      }
+    }
+  }
+}
+
 template <int G, int NQ, int C, int KS, bool SILU>
 __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
   constexpr int NA = SILU ? 2 * NQ : NQ;  // quads per unit: NQ (gate) quads, then their up quads
-  constexpr int P = SILU ? 2 : 1;
-  constexpr int V = NQ * G * 4 * P;  // values per lane: v = ((q * G + g) * 4 + i) * P + u
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -592,77 +673,99 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
     }
   }
 
-  // Sum the 16 blocks: two half-wave swaps halve the values per lane, then
-  // lanes 4 and 8 apart within each row of 16 are added (the lanes of one
-  // quad row stay apart).  V / 4 is even with silu_mul, so a gate value and
-  // its up value stay in one lane.
-  float v[V];
+  blk_finish<G, NQ, KS, SILU>(p, acc, row, rv, gs, lane, wave, kw);
+}
+
+// The same 4x4 block scheme for BF16 weights (no dequant, no block scales):
+// a unit is NQ groups of 4 consecutive rows; lane 4b+j loads 16 bytes of row
+// j, k = 128s + 8b .. +7 of 128-k piece s (256 contiguous bytes of each of the
+// 4 rows per load), the B operand of 2 MFMAs; lane 4b+i brings the same 8 k of
+// token i from LDS.  The KS waves split the pieces; a wave stages all of its
+// activations in LDS first (XS chunks per token, zeros past its pieces), then
+// streams its weights R pieces at a time, the next R in flight while it
+// multiplies the current ones.
+template <int NQ, int R, int KS>
+__global__ __launch_bounds__(256) void k_gemv_blkh(const GemvParams p, int xs) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kw = wave % KS;
+  const int64_t unit = static_cast<int64_t>(xcd_logical_block()) * (4 / KS) + wave / KS;
+  const int jr = lane & 3;
+  const int blk = lane >> 2;
+  const uint32_t row_bytes = static_cast<uint32_t>(p.K) * 2;
+  const uint32_t ldx_bytes = static_cast<uint32_t>(p.ldx) * 2;
+  const rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+  const rsrc_t rx = make_rsrc(p.x, p.x_bytes);
+
+  int64_t row[NQ];
+  bool rv[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int u = 0; u < P; ++u) v[((q * G + g) * 4 + i) * P + u] = acc[u * NQ + q][g][i];
-#pragma unroll
-  for (int j = 0; j < V / 2; ++j) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
-                                                    __builtin_bit_cast(uint32_t, v[j + V / 2]), false, false);
-    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  for (int q = 0; q < NQ; ++q) {
+    row[q] = unit * (4 * NQ) + 4 * q + jr;
+    rv[q] = row[q] < p.N && unit < p.units;
   }
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[j]),
-                                                    __builtin_bit_cast(uint32_t, v[j + V / 4]), false, false);
-    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
-  }
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    v[j] += dpp_f32<0x124>(v[j]);  // row_ror:4
-    v[j] += dpp_f32<0x128>(v[j]);  // row_ror:8
-  }
-  if constexpr (KS > 1) {
-    __shared__ float red[4][V / 4][64];
-    if (kw > 0) {
-#pragma unroll
-      for (int j = 0; j < V / 4; ++j) red[wave][j][lane] = v[j];
+  const int pieces = (p.K + 127) / 128;
+  const int pw = (pieces + KS - 1) / KS;  // pieces per wave
+  const int pc0 = kw * pw;                // this wave's first piece
+  const int npc = pc0 < pieces ? (pieces - pc0 < pw ? pieces - pc0 : pw) : 0;
+  const int rounds = (npc + R - 1) / R;
+  const uint32_t k0 = static_cast<uint32_t>(pc0) * 128;
+
+  // activations: token t's chunk c (8 k) of this wave's slice at t * xs + c;
+  // xs = 64 * (1 KB loads per token) + 4 with the loads covering every round's
+  // pieces (zeros past the wave's), so no token's loads reach the next token's
+  // chunks, and a ds_read_b128 pass (4 tokens, 4 consecutive chunks) hits
+  // distinct banks
+  extern __shared__ u32x4 xdyn[];
+  u32x4* xw = xdyn + wave * 4 * xs;
+  const int nx = (xs - 4) / 64;  // 1 KB loads per token
+  for (int t = 0; t < 4; ++t)
+    for (int d = 0; d < nx; ++d) {
+      const uint32_t c = static_cast<uint32_t>(d) * 64 + lane;
+      const uint32_t k = k0 + c * 8;
+      bload16_lds(rx, xw + t * xs + d * 64,
+                  off_if(c < static_cast<uint32_t>(npc) * 16 && k < static_cast<uint32_t>(p.K) && t < p.M,
+                         static_cast<uint32_t>(t) * ldx_bytes + k * 2));
     }
-    __syncthreads();
-    if (kw == 0) {
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto issue = [&](u32x4 (&w)[R][NQ], int r) {
 #pragma unroll
-      for (int s2 = 1; s2 < KS; ++s2)
+    for (int i = 0; i < R; ++i) {
+      const int pc = r * R + i;  // piece within the wave
 #pragma unroll
-        for (int j = 0; j < V / 4; ++j) v[j] += red[wave + s2][j][lane];
+      for (int q = 0; q < NQ; ++q)
+        w[i][q] = bload16_nt(rw, off_if(rv[q] && pc < npc,
+                                        static_cast<uint32_t>(row[q]) * row_bytes + (k0 + pc * 128 + 8 * blk) * 2));
     }
-  }
-  // lane l now holds values base + 0 .. V/4 - 1 of its quad row l % 4
-  const int base = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4);
-  if (kw == 0 && (lane & 12) == 0) {
+  };
+  f32x4 acc[NQ][1];
 #pragma unroll
-    for (int j = 0; j < V / 4 / P; ++j) {
-      const int t = (base + j * P) / P;
-      const int q = t / (4 * G), m = t % (4 * G);
-      // the row is selected, not indexed: a lane-dependent index into row[]
-      // would move the array to scratch
-      int64_t r = row[0];
-      bool ok = rv[0];
+  for (int q = 0; q < NQ; ++q) acc[q][0] = f32x4{0, 0, 0, 0};
+  auto compute = [&](const u32x4 (&w)[R][NQ], int r) {
 #pragma unroll
-      for (int q2 = 1; q2 < NQ; ++q2)
-        if (q == q2) {
-          r = row[q2];
-          ok = rv[q2];
-        }
-      if (!ok || m >= p.M) continue;
-      if constexpr (!SILU) {
-        p.out[m * static_cast<int64_t>(p.N) + r] = f32_to_bf16_bits(v[j] * gs);
-      } else {
-        const float gv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P] * gs));
-        const float uv = bf16_bits_to_f32(f32_to_bf16_bits(v[j * P + 1] * gs));
-        p.out[m * static_cast<int64_t>(p.half) + r] = f32_to_bf16_bits(silu_f32(gv) * uv);
+    for (int i = 0; i < R; ++i) {
+      const u32x4 xa = xw[jr * xs + (r * R + i) * 16 + blk];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        acc[q][0] = mfma_4x4x4(u32x2{xa.x, xa.y}, u32x2{w[i][q].x, w[i][q].y}, acc[q][0]);
+        acc[q][0] = mfma_4x4x4(u32x2{xa.z, xa.w}, u32x2{w[i][q].z, w[i][q].w}, acc[q][0]);
       }
     }
+  };
+  u32x4 wa[R][NQ], wb[R][NQ];
+  issue(wa, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  vm_wait<R * NQ>();  // the activation loads (issued first) are in LDS
+  for (int r = 0; r < rounds; r += 2) {
+    if (r + 1 < rounds) issue(wb, r + 1);
+    compute(wa, r);
+    if (r + 1 >= rounds) break;
+    if (r + 2 < rounds) issue(wa, r + 2);
+    compute(wb, r + 1);
   }
+  blk_finish<1, NQ, KS, false>(p, acc, row, rv, 1.0f, lane, wave, kw);
 }
 
 // ------------------------------------------------------------------ MFMA
@@ -1445,15 +1548,51 @@ hipError_t launch_blk(const GemvParams& p, hipStream_t stream) {
   }
 }
 
+// BF16 rows of up to kBlkhMaxK columns: at most 28 pieces of 128 k per
+// wave, whose 1 KB activation loads (7 per token) and two rounds of 4 pieces
+// (32 weight loads at 4 groups) stay within vmcnt's count, and whose staged
+// activations (4 tokens x 4 waves x 7 KB) fit the LDS of a compute unit.
+constexpr int kBlkhRound = 4;
+constexpr int64_t kBlkhMaxK = 14336;
+
+template <int NQ>
+hipError_t launch_blkh_nq(GemvParams p, hipStream_t stream) {
+  constexpr int KS = 4;
+  p.units = (p.units + NQ - 1) / NQ;
+  if (t_describe) {
+    std::snprintf(t_describe, t_describe_len, "k_gemv_blkh<%d, %d, %d>", NQ, kBlkhRound, KS);
+    return hipSuccess;
+  }
+  const int64_t pw = ((p.K + 127) / 128 + KS - 1) / KS;                         // pieces per wave
+  const int64_t chunks = (pw + kBlkhRound - 1) / kBlkhRound * kBlkhRound * 16;  // 16 per piece
+  const int xs = static_cast<int>((chunks + 63) / 64 * 64 + 4);
+  const size_t lds = static_cast<size_t>(4) * 4 * xs * 16;
+  hipLaunchKernelGGL((k_gemv_blkh<NQ, kBlkhRound, KS>), dim3(static_cast<unsigned>(p.units)), dim3(256), lds, stream,
+                     p, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_blkh(const GemvParams& p, hipStream_t stream) {
+  switch (blk_quads_per_unit(p.units)) {
+    case 1: return launch_blkh_nq<1>(p, stream);
+    case 2: return launch_blkh_nq<2>(p, stream);
+    case 3: return launch_blkh_nq<3>(p, stream);
+    default: return launch_blkh_nq<4>(p, stream);
+  }
+}
+
 template <bool FP4, bool SILU>
 hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
   const int64_t limit = SILU ? p.half : p.N;
-  if constexpr (FP4) {
-    if (path == kPathBlk) {
+  if (path == kPathBlk) {
+    if constexpr (FP4) {
       p.tiles = p.K / 64;
       p.units = ((limit + 127) / 128) * 32;
       if (p.M <= 4) return launch_blk<1, SILU>(p, stream);
       return launch_blk<2, SILU>(p, stream);
+    } else if constexpr (!SILU) {
+      p.units = (p.N + 3) / 4;  // groups of 4 consecutive rows
+      return launch_blkh(p, stream);
     }
   }
   if (path == kPathValu) {
@@ -1516,7 +1655,7 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
     //    E.g. 4096 x 14336 NVFP4 at 32 tokens 21.4 -> 17.4 us, BF16 36.5 ->
     //    31.6 us; the 4096 x 4096 and 6144 x 4096 sweep shapes never split.
     // the VALU and 4x4 block kernels take these
-    if (fp4 && (M <= kValuMaxMFp4 || default_gemv_path(fp4, M, N, K, silu) == kPathBlk)) return none;
+    if ((fp4 && M <= kValuMaxMFp4) || default_gemv_path(fp4, M, N, K, silu) == kPathBlk) return none;
     const int64_t cus = device_cu_count();
     const double w_tile = 16.0 * (silu ? 2 : 1) * static_cast<double>(K) * (fp4 ? 0.5625 : 2.0);
     const double a_wg = static_cast<double>(xt) * static_cast<double>(K) * 2.0;
@@ -1546,7 +1685,10 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
 
 // NVFP4: the VALU kernel at one token (and at two for rows longer than
 // kBlkMaxK columns), the 4x4 block MFMA kernel from 2 to 4 tokens (rows of
-// up to kBlkMaxK columns), the 16x16 MFMA kernels above.  NVFP4 rows of up
+// up to kBlkMaxK columns), the 16x16 MFMA kernels above.  BF16 without
+// silu_mul: the 4x4 block kernel from 1 to 4 tokens (rows of up to kBlkhMaxK
+// columns), else the MFMA kernels, or the VALU kernel at one token beyond
+// 8192 columns.  NVFP4 rows of up
 // to kVchunkMaxK columns take the chunked VALU kernel (M <= 4 when forced);
 // other VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
 // W4A16_GEMV_PATH=valu|mfma|blk forces a path where it applies (the tests
@@ -1556,7 +1698,9 @@ namespace {
 bool valu_fits(bool fp4, int64_t M, int64_t K) {
   return (fp4 && K <= kVchunkMaxK) ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
 }
-bool blk_fits(bool fp4, int64_t M, int64_t K) { return fp4 && K <= kBlkMaxK && M <= kBlkMaxM; }
+bool blk_fits(bool fp4, int64_t M, int64_t K, int silu) {
+  return fp4 ? (K <= kBlkMaxK && M <= kBlkMaxM) : (!silu && K <= kBlkhMaxK && M <= 4);
+}
 
 }  // namespace
 
@@ -1567,8 +1711,10 @@ int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   // 14.4, 4 tokens 4.86 / 6.51 / 19.9 (16x16 MFMA) -> 4.42 / 5.58 / 14.9; at
   // 5..8 tokens the 16x16 MFMA kernels stay ahead (4x4x4 MFMAs are a
   // quarter of their rate per product, and 8 tokens' activations halve the
-  // workgroups per compute unit)
-  if (blk_fits(fp4, M, K) && M >= 2 && M <= 4) return kPathBlk;
+  // workgroups per compute unit).  BF16 weights, 1..4 tokens (4096 x 4096 /
+  // 4096 x 14336 / 1024 x 14336): 1 token 7.95 / 23.5 (VALU) -> 7.77 / 20.8,
+  // 4 tokens 8.26 / 25.0 / 22.0 (16x16 MFMA) -> 7.92 / 21.0 / 9.0
+  if (blk_fits(fp4, M, K, silu) && M >= (fp4 ? 2 : 1) && M <= 4) return kPathBlk;
   // BF16 at M = 1: the MFMA path up to K = 8192 (measured 5% faster at
   // 4096), the VALU path beyond (2% faster at 14336)
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : (K <= 8192 ? 0 : 1);
@@ -1579,7 +1725,7 @@ int choose_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   if (const char* env = std::getenv("W4A16_GEMV_PATH")) {
     if (std::strcmp(env, "mfma") == 0) return kPathMfma;
     if (std::strcmp(env, "valu") == 0 && valu_fits(fp4, M, K)) return kPathValu;
-    if (std::strcmp(env, "blk") == 0 && blk_fits(fp4, M, K)) return kPathBlk;
+    if (std::strcmp(env, "blk") == 0 && blk_fits(fp4, M, K, silu)) return kPathBlk;
   }
   return default_gemv_path(fp4, M, N, K, silu);
 }
