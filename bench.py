@@ -356,7 +356,7 @@ CROSSOVER_M = [32, 48, 64, 80, 96, 128, 192, 256]
 
 def dispatch_table() -> int:
     """Per (weight, N, K, silu_mul, M): µs per call of the default dispatch,
-    of each path forced with W4A16_GEMV_PATH, and of the split-K entry point
+    of each path (valu, mfma, blk) forced with W4A16_GEMV_PATH, and of the split-K entry point
     where its plan splits, with the kernel each one launches (graphs of 64
     launches over rotating weight copies, timed in turns: the median of 3
     rounds).  Then the crossover of the GEMV (up to its 192-token limit) and the
@@ -407,7 +407,7 @@ def dispatch_table() -> int:
                     raise RuntimeError(f"GEMV failed: {lib.w4a16_last_error().decode()}")
             rec = {"weight": wfmt, "N": n, "K": k, "silu_mul": silu, "M": m}
             graphs = {}
-            for path in ("default", "valu", "mfma", "splitk"):
+            for path in ("default", "valu", "mfma", "blk", "splitk"):
                 if path in ("default", "splitk"):
                     os.environ.pop("W4A16_GEMV_PATH", None)
                 else:
@@ -415,6 +415,9 @@ def dispatch_table() -> int:
                 kern = gemv_kernel_name(m, n, k, silu, fp4, splitk=path == "splitk")
                 if path == "valu" and not kern.startswith(("k_gemv_vchunk", "k_gemv_valu")):
                     rec[path] = None  # no VALU kernel at this M
+                    continue
+                if path == "blk" and not kern.startswith("k_gemv_blk"):
+                    rec[path] = None  # no 4x4 block kernel at this M
                     continue
                 if path == "splitk" and kern == gemv_kernel_name(m, n, k, silu, fp4):
                     rec[path] = None  # the plan does not split here
@@ -443,7 +446,7 @@ def dispatch_table() -> int:
                 rec[path] = {"kernel": kern, "us": round(sorted(us[path])[1], 3)}
             del graphs
             os.environ.pop("W4A16_GEMV_PATH", None)
-            times = [rec[p]["us"] for p in ("valu", "mfma") if rec[p]]
+            times = [rec[p]["us"] for p in ("valu", "mfma", "blk") if rec[p]]
             rec["default_is_fastest_path"] = rec["default"]["us"] <= min(times) * 1.02
             best_default += rec["default_is_fastest_path"]
             rows.append(rec)

@@ -200,9 +200,16 @@ def test_gemv_kernel_name_query(monkeypatch):
     for m in (2, 4):  # with silu_mul: units of 4 or 3 gate quads and their up quads
         assert gemv_kernel_name(m, 28672, 4096, silu_mul=True) == "k_gemv_blk<1, 4, 2, 4, true>"
         assert gemv_kernel_name(m, 2 * 6144, 4096, silu_mul=True) == "k_gemv_blk<1, 3, 2, 4, true>"
+    # 5..8 tokens: the 4x4 kernel with two token groups where its units fill the
+    # compute units in one round
+    for m in (5, 8):
+        assert gemv_kernel_name(m, 4096, 4096) == "k_gemv_blk<2, 4, 2, 4, false>"
+        assert gemv_kernel_name(m, 256, 1024) == "k_gemv_blk<2, 1, 1, 4, false>"
+    assert gemv_kernel_name(8, 4096, 4096, silu_mul=True).startswith("k_gemv_mfma<true, 8, true,")
     # the MFMA kernels are named by the token rows they stage per step
-    for m, xt in ((5, 8), (8, 8), (9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
+    for m, xt in ((9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 4096, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
+    assert gemv_kernel_name(8, 4096, 8192).startswith("k_gemv_mfma<true, 8, false,")  # K > 4096
     for m, xt in ((9, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
         assert gemv_kernel_name(m, 6144, 4096).startswith(f"k_gemv_mfma<true, {xt}, false,")
     # 5..8 tokens where 24-row units fit the compute units and 16-row tiles do not
@@ -275,7 +282,8 @@ def test_splitk_plan_and_workspace_size(monkeypatch):
         nt = max(1, xt // 16)
         assert gemv_kernel_name(m, 1024, 8192, splitk=True) == f"k_gemv_mfma<true, {xt}, false, 1, 4>"
         assert lib.gemv_splitk_workspace_bytes(1, m, 1024, 8192, 0) == 65536 + 64 * 4 * nt * 1024
-    assert gemv_kernel_name(8, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 8, false, 1, 1>"  # too little work
+    assert gemv_kernel_name(9, 1024, 2048, splitk=True) == "k_gemv_mfma<true, 16, false, 1, 1>"  # too little work
+    assert gemv_kernel_name(8, 1024, 4096, splitk=True) == "k_gemv_blk<2, 1, 2, 4, false>"  # the 4x4 kernel: no split
     assert gemv_kernel_name(4, 1024, 4096, splitk=True) == "k_gemv_blk<1, 1, 2, 4, false>"  # the 4x4 kernel: no split
     assert gemv_kernel_name(32, 1024, 4096, splitk=True) == "k_gemv_mfma<true, 32, false, 1, 2>"
     assert gemv_kernel_name(32, 4096, 14336, splitk=True) == "k_gemv_mfma<true, 32, false, 2, 2>"

@@ -122,16 +122,20 @@ def test_nvfp4_gemv_long_rows(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, d["gs"][0], k, f"nvfp4_gemv M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("m", [2, 3, 4])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 8])
 @pytest.mark.parametrize("n,nq", [(48, 1), (2048, 2), (3072, 3), (4096, 4), (6144, 3)])
 @pytest.mark.parametrize("k,c", [(64, 1), (1536, 1), (2560, 2), (4096, 2)])
 def test_nvfp4_gemv_4x4_block_kernel(m, n, nq, k, c, monkeypatch):
-    """The 4x4 block MFMA kernel at 2..4 tokens: every unit size the dispatch
-    picks (1..4 quads, units that cross 128-row bands at 3), one or two
-    512-k segments per lane, ragged K (waves and lanes past the end of a row),
-    a partial band (48 rows), every output checked."""
+    """The 4x4 block MFMA kernel at 2..8 tokens (one or two groups of 4):
+    every unit size the dispatch picks (1..4 quads, units that cross 128-row
+    bands at 3), one or two 512-k segments per lane, ragged K (waves and
+    lanes past the end of a row), a partial band (48 rows), every output
+    checked.  At 5..8 tokens it serves only where its units fit one round."""
     monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
-    assert lib.gemv_kernel_name(m, n, k) == f"k_gemv_blk<1, {nq}, {c}, 4, false>"
+    if m > 4 and n == 6144:
+        assert lib.gemv_kernel_name(m, n, k) == "k_gemv_mfma_bd<false, 8, 24>"
+    else:
+        assert lib.gemv_kernel_name(m, n, k) == f"k_gemv_blk<{1 if m <= 4 else 2}, {nq}, {c}, 4, false>"
     _say("nvfp4_gemv blk", m, n, k)
     d = synth.dense_w4a16(m, n, k, seed=synth.seed_for(0, m) + 3 * n + k)
     got = run_nvfp4(d, n)

@@ -1715,6 +1715,14 @@ int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   // 4096 x 14336 / 1024 x 14336): 1 token 7.95 / 23.5 (VALU) -> 7.77 / 20.8,
   // 4 tokens 8.26 / 25.0 / 22.0 (16x16 MFMA) -> 7.92 / 21.0 / 9.0
   if (blk_fits(fp4, M, K, silu) && M >= (fp4 ? 2 : 1) && M <= 4) return kPathBlk;
+  // NVFP4 without silu_mul at 5..8 tokens: the 4x4 kernel where its units fill
+  // the compute units in one round (4096 x 4096: 5.13 -> 5.00 us at 8 tokens;
+  // at 6144 x 4096, two units per compute unit, 6.43 -> 6.72)
+  if (fp4 && !silu && blk_fits(fp4, M, K, silu) && M > 4) {
+    const int64_t quads = (N + 127) / 128 * 32;
+    const int nq = blk_quads_per_unit(quads);
+    if ((quads + nq - 1) / nq <= device_cu_count()) return kPathBlk;
+  }
   // BF16 at M = 1: the MFMA path up to K = 8192 (measured 5% faster at
   // 4096), the VALU path beyond (2% faster at 14336)
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : (K <= 8192 ? 0 : 1);
