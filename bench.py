@@ -71,7 +71,8 @@ def log(*a):
 
 
 # the sources the dense GEMV kernels are compiled from
-GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp", "chunk_core.hpp", "launch.hpp"]
+GEMV_SOURCES = ["gemv.hip", "device_common.hpp", "mfma_core.hpp", "unit_core.hpp", "chunk_core.hpp", "blk_core.hpp",
+                "launch.hpp"]
 
 
 def source_digest(csrc: str | None = None) -> str:

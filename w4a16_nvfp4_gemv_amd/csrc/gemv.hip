@@ -28,6 +28,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "blk_core.hpp"
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_core.hpp"
@@ -449,36 +450,23 @@ __global__ __launch_bounds__(256) void k_gemv_vchunk(const GemvParams p) {
 }
 
 // ------------------------------------------------------------------ 4x4 block MFMA (NVFP4, M <= 8)
-// v_mfma_f32_4x4x4_16b_bf16 computes 16 independent 4x4x4 products, block
-// b on lanes 4b..4b+3: lane 4b+i holds row i of block b's A (4 k), lane
-// 4b+j column j of its B, and the result C[i][j] lands in item i of lane
-// 4b+j.  Here the 16 blocks are 16 k ranges of the same rows, so a unit of
-// quads {r, r+32, r+64, r+96} streams like the VALU kernel: lane 4b+j loads
-// 16 bytes of row j at byte 16b of a 256-byte stretch (one load of the wave
-// reads 256 contiguous bytes of each of the 4 rows), i.e. 32 codes, k =
-// 512s + 32b .. +31 of 512-k segment s.  Those codes are the B operand of 8
-// MFMAs (4 k each) against the A operand of tokens 4g..4g+3 (lane 4b+i:
-// token 4g+i, the same 32 k: 64 contiguous activation bytes).  Each MFMA
-// chain covers 16 k, one E4M3 block, and is scaled once into the FP32
-// accumulator, as the VALU kernel scales its chunk sums; the 16 blocks are
-// added across lanes at the end.  NQ quads per unit (2: rows r and r + 1 of
-// each quad position, whose scale chunks share a cache line), G groups of 4
-// tokens, C segments per lane, KS waves splitting K.  All loads are issued
-// up front.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma_4x4x4(u32x2 a, u32x2 b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0,
-                                                0);
-}
-
-// The end of a 4x4 block kernel: acc[a][g] holds, in item i of lane 4b+j,
-// block b's partial sum for row j of quad a and token 4g+i.  Sums the 16
-// blocks (two half-wave swaps halve the values per lane, then lanes 4 and 8
-// apart within each row of 16 are added, so the lanes of one quad row stay
-// apart; V / 4 is even with silu_mul, so a gate value and its up value stay
-// in one lane), adds the KS waves of the unit in slice order through LDS and
-// stores the rows (row[q], the lane's row of quad q).
+// On v_mfma_f32_4x4x4_16b_bf16 (blk_core.hpp), a unit of quads {r, r+32,
+// r+64, r+96} streams like the VALU kernel: lane 4b+j loads 16 bytes of row j
+// at byte 16b of a 256-byte stretch (one load of the wave reads 256
+// contiguous bytes of each of the 4 rows), i.e. 32 codes, k = 512s + 32b ..
+// +31 of 512-k segment s.  Those codes are the B operand of 8 MFMAs (4 k
+// each) against the A operand of tokens 4g..4g+3 (lane 4b+i: token 4g+i, the
+// same 32 k: 64 contiguous activation bytes).  Each MFMA chain covers 16 k,
+// one E4M3 block, and is scaled once into the FP32 accumulator, as the VALU
+// kernel scales its chunk sums; the 16 blocks are added across lanes at the
+// end.  NQ adjacent quads per unit (their scale chunks share cache lines), G
+// groups of 4 tokens, C segments per lane, KS waves splitting K.  All loads
+// are issued up front.
+//
+// The end of a dense 4x4 block kernel: acc[a][g] holds, in item i of lane
+// 4b+j, block b's partial sum for row j of quad a and token 4g+i.  Sums the
+// blocks and waves (blk_reduce; with silu_mul a gate value and its up value
+// stay in one lane) and stores the rows (row[q], the lane's row of quad q).
 template <int G, int NQ, int KS, bool SILU>
 __device__ __forceinline__ void blk_finish(const GemvParams& p, const f32x4 (&acc)[SILU ? 2 * NQ : NQ][G],
                                            const int64_t (&row)[SILU ? 2 * NQ : NQ], const bool (&rv)[SILU ? 2 * NQ : NQ],
@@ -494,39 +482,7 @@ __device__ __forceinline__ void blk_finish(const GemvParams& p, const f32x4 (&ac
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int u = 0; u < P; ++u) v[((q * G + g) * 4 + i) * P + u] = acc[u * NQ + q][g][i];
-#pragma unroll
-  for (int j = 0; j < V / 2; ++j) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
-                                                    __builtin_bit_cast(uint32_t, v[j + V / 2]), false, false);
-    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
-  }
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v[j]),
-                                                    __builtin_bit_cast(uint32_t, v[j + V / 4]), false, false);
-    v[j] = __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
-  }
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    v[j] += dpp_f32<0x124>(v[j]);  // row_ror:4
-    v[j] += dpp_f32<0x128>(v[j]);  // row_ror:8
-  }
-  if constexpr (KS > 1) {
-    __shared__ float red[4][V / 4][64];
-    if (kw > 0) {
-#pragma unroll
-      for (int j = 0; j < V / 4; ++j) red[wave][j][lane] = v[j];
-    }
-    __syncthreads();
-    if (kw == 0) {
-#pragma unroll
-      for (int s2 = 1; s2 < KS; ++s2)
-#pragma unroll
-        for (int j = 0; j < V / 4; ++j) v[j] += red[wave + s2][j][lane];
-    }
-  }
-  // lane l now holds values base + 0 .. V/4 - 1 of its quad row l % 4
-  const int base = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4);
+  const int base = blk_reduce<V, KS>(v, lane, wave, kw);
   if (kw == 0 && (lane & 12) == 0) {
 #pragma unroll
     for (int j = 0; j < V / 4 / P; ++j) {
@@ -643,33 +599,11 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
       u32x2 wb[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wv[c][a][d];
-        wb[2 * d] = u32x2{e2m1x2_bf16<0>(w), e2m1x2_bf16<1>(w)};
-        wb[2 * d + 1] = u32x2{e2m1x2_bf16<2>(w), e2m1x2_bf16<3>(w)};
-      }
+      blk_codes(wv[c][a], wb);
       const float s0 = e4m3_to_f32<0>(sw[c][a] >> shift);
       const float s1 = e4m3_to_f32<1>(sw[c][a] >> shift);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        f32x4 h0 = f32x4{0, 0, 0, 0}, h1 = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const u32x4& xa = xv[c][g][st / 2];
-          h0 = mfma_4x4x4(st % 2 ? u32x2{xa.z, xa.w} : u32x2{xa.x, xa.y}, wb[st], h0);
-        }
-#pragma unroll
-        for (int st = 4; st < 8; ++st) {
-          const u32x4& xa = xv[c][g][st / 2];
-          h1 = mfma_4x4x4(st % 2 ? u32x2{xa.z, xa.w} : u32x2{xa.x, xa.y}, wb[st], h1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[a][g][i] = __builtin_fmaf(h0[i], s0, acc[a][g][i]);
-          acc[a][g][i] = __builtin_fmaf(h1[i], s1, acc[a][g][i]);
-        }
-      }
+      for (int g = 0; g < G; ++g) blk_mac(wb, xv[c][g], s0, s1, acc[a][g]);
     }
   }
 
