@@ -12,14 +12,14 @@ replayed from HIP graphs are timed beside them for comparison.
 
 value = algorithmic bytes of a step (packed weight + flat scale bytes of the
 12 calls) / wall time per step, in GB/s.  Activation and output bytes are not
-counted.  Each per-call figure comes from HIP events around a graph of 64
-back-to-back launches of that one call shape on the stream the graph runs
-on.  The roofline object reports the kernel with the largest share of the
-step, with its HBM traffic from the committed rocprofv3 counter runs when
-they were taken on the current kernel sources.  Each per-call entry also
-carries the eager-launch time of the same 64 launches and the time of a
-streaming-read reference that reads the same weight and scale copies and
-nothing else (probe/read_floor.hip), as `floor_us` and `frac_of_floor`.  The CPU baseline is the
+counted.  Each per-call figure comes from HIP events around 64 back-to-back
+eager launches of that one call shape on their stream (a sleep kernel holds
+the stream while the host enqueues them).  The roofline object reports the
+kernel with the largest share of the step, with its HBM traffic from the
+committed rocprofv3 counter runs when they were taken on the current kernel
+sources.  Each per-call entry also carries the time of a streaming-read
+reference that reads the same weight and scale copies and nothing else
+(probe/read_floor.hip), as `floor_us` and `frac_of_floor`.  The CPU baseline is the
 binary64 oracle on the host cores over whole steps of the same workload.
 The "extras" list times the other workloads of the family (fused gate|up
 SiLU GEMV, BF16-weight GEMV, MoE decode pair) the same way; they are not
@@ -239,8 +239,9 @@ def eager_us_per_launch(torch, stream, launch_i, n_launch: int) -> float:
         with torch.cuda.stream(stream):
             torch.cuda._sleep(max(2_000_000, 50_000 * n_launch))  # longer than the host needs to enqueue
         a.record(stream)
-        for i in range(n_launch):
-            launch_i(i, stream.cuda_stream)
+        with torch.cuda.stream(stream):  # (launches that take the current stream)
+            for i in range(n_launch):
+                launch_i(i, stream.cuda_stream)
         b.record(stream)
         torch.cuda.synchronize()
         if r:
@@ -319,8 +320,8 @@ def silu_counter_pass() -> int:
 def read_floor_mode() -> int:
     """Times the streaming-read reference alone: the weight + scale bytes of
     every call shape of the benchmark and a sweep of sizes, each over rotating
-    copies (more than 600 MB) in graphs of 64 launches.  One JSON line per
-    size."""
+    copies (more than 600 MB), 64 launches back to back (as the per-call
+    figures).  One JSON line per size."""
     import torch
 
     import synth
@@ -338,7 +339,7 @@ def read_floor_mode() -> int:
         n = max(2, int(600e6 // (wb + sb)) + 1)
         ws = [torch.randint(0, 256, (wb,), dtype=torch.uint8, device=dev) for _ in range(n)]
         ss = [torch.randint(0, 256, (max(sb, 16),), dtype=torch.uint8, device=dev) for _ in range(n)] if sb else None
-        us = graph_us_per_launch(torch, cap, floor_launcher(rf, torch, dev, ws, ss, wb, sb), 64)
+        us = eager_us_per_launch(torch, cap, floor_launcher(rf, torch, dev, ws, ss, wb, sb), 64)
         rec = {"read_floor": name, "bytes": wb + sb, "us": round(us, 3), "GBps": round((wb + sb) / us / 1e3, 1),
                "frac_peak": round((wb + sb) / us / 1e3 / PEAK_GBPS, 4), "workgroups": int(rf.read_floor_blocks(wb, sb, floor_nl(wb + sb)))}
         print(json.dumps(rec), flush=True)
@@ -627,6 +628,14 @@ def main() -> int:
     log(f"graph replay: {graph_us:.2f} us/step")
 
     # ---------------------------------------------------------------- per call
+    # Per-call figures: back-to-back eager launches on the stream they run on
+    # (a kernel tracer times graph-replayed kernels one by one, without the
+    # overlap of consecutive launches, so eager launches are the ones its
+    # durations can be compared with; replayed from graphs, the same 64
+    # launches measured within 2% of these).
+    def time_call(launch_i, n_launch: int) -> float:
+        return eager_us_per_launch(torch, cap, launch_i, n_launch)
+
     def time_graph(launch_i, n_launch: int) -> float:
         return graph_us_per_launch(torch, cap, launch_i, n_launch)
 
@@ -635,21 +644,19 @@ def main() -> int:
     rf = read_floor_lib()
     floors = {}
     for c in calls:
-        us = time_graph(lambda i, h, c=c: launch(c, i % n_copies, h), L)
+        us = time_call(lambda i, h, c=c: launch(c, i % n_copies, h), L)
         nbytes = algorithmic_bytes(c["n"], c["k"])
-        us_eager = eager_us_per_launch(torch, cap, lambda i, h, c=c: launch(c, i % n_copies, h), L)
         key = (c["n"], c["k"])
         if key not in floors:
             # the streaming-read reference over the same weight and scale copies
-            floors[key] = time_graph(floor_launcher(rf, torch, dev, c["w"], c["s"], c["n"] * c["k"] // 2,
-                                                    c["s"][0].numel()), L)
+            floors[key] = time_call(floor_launcher(rf, torch, dev, c["w"], c["s"], c["n"] * c["k"] // 2,
+                                                   c["s"][0].numel()), L)
         per_call.append({"N": c["n"], "K": c["k"], "M": c["m"], "kernel": c["kernel"],
                          "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                          "frac_peak": round(nbytes / us / 1e3 / PEAK_GBPS, 4), "bytes": nbytes,
-                         "floor_us": round(floors[key], 3), "frac_of_floor": round(floors[key] / us, 4),
-                         "us_eager": round(us_eager, 3)})
+                         "floor_us": round(floors[key], 3), "frac_of_floor": round(floors[key] / us, 4)})
         log(f"N={c['n']} K={c['k']} M={c['m']:2d}: {us:7.3f} us/call {nbytes / us / 1e3:8.1f} GB/s  "
-            f"(eager {us_eager:.3f} us, read floor {floors[key]:.3f} us)  {c['kernel']}")
+            f"(read floor {floors[key]:.3f} us)  {c['kernel']}")
 
     # dominant kernel: largest share of the step's time
     share = {}
@@ -673,7 +680,7 @@ def main() -> int:
         c["w"] = c["s"] = None
     torch.cuda.empty_cache()
 
-    extras = [] if args.no_extras else run_extras(torch, dev, lib, cap, time_graph)
+    extras = [] if args.no_extras else run_extras(torch, dev, lib, cap, time_call, time_graph)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -711,7 +718,7 @@ def main() -> int:
     return 0
 
 
-def run_extras(torch, dev, lib, cap, time_graph) -> list:
+def run_extras(torch, dev, lib, cap, time_call, time_graph) -> list:
     """Per-call timings of the other workloads (not part of the step)."""
     import synth
     from w4a16_nvfp4_gemv_amd import gemv_kernel_name, moe_down_combine, moe_gate_up
@@ -733,7 +740,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
         def f(i, h, m=m, x=x, gs=gs, o=o):
             assert lib.nvfp4_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), ss[i % nc].data_ptr(),
                                   gs.data_ptr(), n, 1, o.data_ptr(), h) == 0
-        us = time_graph(f, 32)
+        us = time_call(f, 32)
         nb = algorithmic_bytes(n, k)
         out.append({"workload": "nvfp4_gemv silu_mul", "N": n, "K": k, "M": m, "kernel": gemv_kernel_name(m, n, k, True),
                     "us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb})
@@ -752,7 +759,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
 
             def f(i, h, m=m, x=x, o=o, n=n, k=k):
                 assert lib.bf16_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), n, 0, o.data_ptr(), h) == 0
-            us = time_graph(f, 32)
+            us = time_call(f, 32)
             nb = n * k * 2
             out.append({"workload": "bf16_gemv", "N": n, "K": k, "M": m,
                         "kernel": gemv_kernel_name(m, n, k, weight_fp4=False),
@@ -801,7 +808,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
             dc(i, h)
         distinct = sum(len(set(t["ids"].flatten().tolist())) for t in sets) / len(sets)
         for name, fn, nb in (("moe_gate_up", gu, distinct * w1_e + sh1), ("moe_down_combine", dc, distinct * w2_e + sh2)):
-            us = time_graph(fn, 32)
+            us = time_call(fn, 32)
             out.append({"workload": name, "M": m, "experts_per_call": round(distinct, 2), "us": round(us, 3),
                         "GBps": round(nb / us / 1e3, 1), "bytes": int(nb)})
             log(f"{name} M={m:2d}: {us:7.3f} us/call {nb / us / 1e3:8.1f} GB/s ({distinct:.1f} experts)")
@@ -866,7 +873,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
                         st = lib.bf16_gemv_splitk(x.data_ptr(), m, k, k, w, n, 0, work.data_ptr(), work.numel(),
                                                   o.data_ptr(), h)
                     assert st == 0, lib.w4a16_last_error()
-                rec["us_" + entry] = round(time_graph(f, 32), 3)
+                rec["us_" + entry] = round(time_call(f, 32), 3)
             rec["GBps"] = round(nb / rec["us_splitk"] / 1e3, 1)
             out.append(rec)
             log(f"{rec['workload']} N={n} K={k} M={m:2d}: {rec['us_plain']:7.3f} us -> {rec['us_splitk']:7.3f} us "
@@ -888,7 +895,7 @@ def run_extras(torch, dev, lib, cap, time_graph) -> list:
             def f(i, h, m=m, x=x, gs=gs, o=o, n=n, k=k):
                 assert lib.nvfp4_gemv(x.data_ptr(), m, k, k, ws[i % nc].data_ptr(), ss[i % nc].data_ptr(),
                                       gs.data_ptr(), n, 0, o.data_ptr(), h) == 0
-            us = time_graph(f, 32)
+            us = time_call(f, 32)
             nb = algorithmic_bytes(n, k)
             out.append({"workload": "nvfp4_gemv", "N": n, "K": k, "M": m, "kernel": gemv_kernel_name(m, n, k),
                         "us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "bytes": nb})
