@@ -220,16 +220,22 @@ def test_gemv_kernel_name_query(monkeypatch):
     assert gemv_kernel_name(8, 28672, 4096, silu_mul=True) == "k_gemv_mfma_bd<true, 8, 56>"
     assert gemv_kernel_name(4, 28672, 8192, silu_mul=True).startswith("k_gemv_mfma<true, 4, true,")
     assert gemv_kernel_name(32, 4096, 14336, weight_fp4=False).startswith("k_gemv_mfma<false, 32, false,")
-    # BF16 at 1..4 tokens: the 4x4 block kernel up to K = 14336 (without silu_mul);
-    # at one token beyond that the VALU kernel
+    # BF16 without silu_mul: the 4x4 block kernel at 1..4 tokens, and at 5..8
+    # for rows longer than 2048 columns; up to 8 pieces of 128 k per wave all
+    # loaded up front (R = 4 or 8), longer rows in rounds of 4
     for m in (1, 4):
-        assert gemv_kernel_name(m, 4096, 4096, weight_fp4=False) == "k_gemv_blkh<4, 4, 4>"
-        assert gemv_kernel_name(m, 4096, 14336, weight_fp4=False) == "k_gemv_blkh<4, 4, 4>"
-    assert gemv_kernel_name(2, 1024, 14336, weight_fp4=False) == "k_gemv_blkh<1, 4, 4>"
-    assert gemv_kernel_name(5, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 8, false,")
+        assert gemv_kernel_name(m, 4096, 4096, weight_fp4=False) == "k_gemv_blkh<1, 4, 8, 4, true>"
+        assert gemv_kernel_name(m, 4096, 14336, weight_fp4=False) == "k_gemv_blkh<1, 4, 4, 4, false>"
+        assert gemv_kernel_name(m, 4096, 16384, weight_fp4=False) == "k_gemv_blkh<1, 4, 4, 4, false>"
+    assert gemv_kernel_name(2, 1024, 14336, weight_fp4=False) == "k_gemv_blkh<1, 1, 4, 4, false>"
+    assert gemv_kernel_name(3, 4096, 1024, weight_fp4=False) == "k_gemv_blkh<1, 4, 4, 4, true>"
+    for m in (5, 8):
+        assert gemv_kernel_name(m, 4096, 4096, weight_fp4=False) == "k_gemv_blkh<2, 4, 8, 4, true>"
+        assert gemv_kernel_name(m, 2048, 8192, weight_fp4=False) == "k_gemv_blkh<2, 2, 4, 4, false>"
+        assert gemv_kernel_name(m, 4096, 2048, weight_fp4=False).startswith("k_gemv_mfma<false, 8, false,")
+    assert gemv_kernel_name(9, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 16, false,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False, silu_mul=True).startswith("k_gemv_mfma<false, 4, true,")
-    assert gemv_kernel_name(1, 4096, 16384, weight_fp4=False).startswith("k_gemv_valu<false, 1,")
-    assert gemv_kernel_name(4, 4096, 16384, weight_fp4=False).startswith("k_gemv_mfma<false, 4, false,")
+    assert gemv_kernel_name(1, 8192, 16384, weight_fp4=False, silu_mul=True).startswith("k_gemv_valu<false, 1, 64, true,")
     monkeypatch.setenv("W4A16_GEMV_PATH", "mfma")
     assert gemv_kernel_name(1, 4096, 4096).startswith("k_gemv_mfma<true, 4, false,")
     for m, tk in ((3, 4), (4, 4)):

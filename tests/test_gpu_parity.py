@@ -548,21 +548,44 @@ def test_bf16_gemv_small_shapes(m, n, k, gemv_path):
     check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("n,nq", [(48, 1), (2048, 2), (3072, 3), (4096, 4)])
-@pytest.mark.parametrize("k", [16, 1040, 1536, 2560, 14336])
+@pytest.mark.parametrize("k", [16, 1040, 1536, 2560, 4096, 14336])
 def test_bf16_gemv_4x4_block_kernel(m, n, nq, k, monkeypatch):
-    """The BF16 4x4 block kernel at 1..4 tokens: every unit size, a piece cut
-    by the end of the row (K % 128 != 0), waves without pieces (K = 16), a
-    last round of fewer pieces (K = 1536, 2560), the longest rows (two rounds
-    in flight, 7 activation loads per token), every output checked."""
-    monkeypatch.delenv("W4A16_GEMV_PATH", raising=False)
-    assert lib.gemv_kernel_name(m, n, k, weight_fp4=False) == f"k_gemv_blkh<{nq}, 4, 4>"
+    """The BF16 4x4 block kernel (forced) at 1..8 tokens: every unit size,
+    one and two token groups, a piece cut by the end of the row (K % 128 !=
+    0), waves without pieces (K = 16), every wave's pieces loaded up front
+    (R = 4 up to 4 pieces per wave, 8 up to 8) and in rounds of 4 (K = 14336,
+    28 pieces per wave, a last round of fewer), every output checked."""
+    monkeypatch.setenv("W4A16_GEMV_PATH", "blk")
+    pw = (-(-k // 128) + 3) // 4  # 128-k pieces per wave
+    r, one = (4, "true") if pw <= 4 else ((8, "true") if pw <= 8 else (4, "false"))
+    g = 1 if m <= 4 else 2
+    assert lib.gemv_kernel_name(m, n, k, weight_fp4=False) == f"k_gemv_blkh<{g}, {nq}, {r}, 4, {one}>"
     _say("bf16_gemv blkh", m, n, k)
     d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 7 * n + k)
     got = run_bf16(d)
     _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"])
     check_gemv(got, acc, absacc, 1.0, k, f"bf16_gemv blkh M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("gemv_path", PATHS, indirect=True)
+@pytest.mark.parametrize("m", [1, 3, 4, 8, 17])
+@pytest.mark.parametrize("k", [144, 336, 1040])
+def test_bf16_gemv_nonfinite_next_row(m, k, gemv_path):
+    """K % 128 != 0, and every odd row starts with 128 infinite weights: a
+    kernel whose last 128-k piece read past the end of an even row would
+    pick them up (times zero activations: NaN).  The even rows must match
+    the oracle; the odd rows' own sums are not finite and are not compared."""
+    n = 64
+    _say("bf16_gemv nonfinite next row", m, n, k, gemv_path)
+    d = synth.dense_bf16(m, n, k, seed=synth.seed_for(3, m) + 11 * k)
+    w = d["w"].clone()
+    w[1::2, :128] = float("inf")
+    d = dict(x=d["x"], w=w)
+    got = run_bf16(d)
+    _, acc, absacc = oracle.bf16_gemv(d["x"], d["w"])
+    check_gemv(got[:, 0::2], acc[:, 0::2], absacc[:, 0::2], 1.0, k, f"bf16_gemv M={m} N={n} K={k} even rows")
 
 
 @pytest.mark.parametrize("m", [1, 4, 16, 32])

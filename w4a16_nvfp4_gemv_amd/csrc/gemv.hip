@@ -11,11 +11,12 @@
 //     or without silu_mul): the same streaming as k_gemv_vchunk (256
 //     contiguous bytes of a row per load, every load issued up front), with
 //     the products on v_mfma_f32_4x4x4_16b_bf16, whose 16 blocks take 16 k
-//     ranges of 4 rows.  k_gemv_blkh is its BF16-weight form (1..4 tokens,
-//     rows of up to 14336 columns, without silu_mul).
+//     ranges of 4 rows.  k_gemv_blkh is its BF16-weight form (1..8 tokens,
+//     without silu_mul; the activations go straight into the MFMA operands).
 //   * k_gemv_valu1 / k_gemv_valu -- the same VALU scheme with lanes owning
-//     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights at M = 1 beyond
-//     14336 columns and NVFP4 rows longer than 16384 columns at M <= 2.
+//     whole 64-k (NVFP4) or 16-k (BF16) tiles: BF16 weights with silu_mul at
+//     M = 1 beyond 8192 columns and NVFP4 rows longer than 16384 columns at
+//     M <= 2.
 //   * k_gemv_mfma -- swap-AB MFMA path (v_mfma_f32_16x16x32_bf16): the 16
 //     weight rows of a tile are the A operand, up to 16 tokens the B operand,
 //     staged through an LDS ring.  The waves of a workgroup split K and
@@ -617,13 +618,17 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
 // The same 4x4 block scheme for BF16 weights (no dequant, no block scales):
 // a unit is NQ groups of 4 consecutive rows; lane 4b+j loads 16 bytes of row
 // j, k = 128s + 8b .. +7 of 128-k piece s (256 contiguous bytes of each of the
-// 4 rows per load), the B operand of 2 MFMAs; lane 4b+i brings the same 8 k of
-// token i from LDS.  The KS waves split the pieces; a wave stages all of its
-// activations in LDS first (XS chunks per token, zeros past its pieces), then
-// streams its weights R pieces at a time, the next R in flight while it
-// multiplies the current ones.
-template <int NQ, int R, int KS>
-__global__ __launch_bounds__(256) void k_gemv_blkh(const GemvParams p, int xs) {
+// 4 rows per load), the B operand of 2 MFMAs.  The activations go straight
+// into the A operands: lane 4b+i of token group g loads token 4g+i's same 8
+// k (one load of the wave reads 256 contiguous bytes of each of 4 token rows),
+// so neither K nor the token count is bound by LDS (staging them in LDS, as
+// the NVFP4 kernel must, measured 0.4-0.8 us slower).  G groups of 4 tokens;
+// the KS waves split the pieces.  ONE: a wave's pieces (at most R) are all
+// loaded up front and multiplied in order as they arrive; else R pieces per
+// round, the next round's weights and activations in flight while the
+// current one is multiplied.
+template <int G, int NQ, int R, int KS, bool ONE>
+__global__ __launch_bounds__(256) void k_gemv_blkh(const GemvParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -649,61 +654,61 @@ __global__ __launch_bounds__(256) void k_gemv_blkh(const GemvParams p, int xs) {
   const int npc = pc0 < pieces ? (pieces - pc0 < pw ? pieces - pc0 : pw) : 0;
   const int rounds = (npc + R - 1) / R;
   const uint32_t k0 = static_cast<uint32_t>(pc0) * 128;
+  uint32_t xo[G];
+  bool xok[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    xo[g] = static_cast<uint32_t>(4 * g + jr) * ldx_bytes;
+    xok[g] = 4 * g + jr < p.M;
+  }
 
-  // activations: token t's chunk c (8 k) of this wave's slice at t * xs + c;
-  // xs = 64 * (1 KB loads per token) + 4 with the loads covering every round's
-  // pieces (zeros past the wave's), so no token's loads reach the next token's
-  // chunks, and a ds_read_b128 pass (4 tokens, 4 consecutive chunks) hits
-  // distinct banks
-  extern __shared__ u32x4 xdyn[];
-  u32x4* xw = xdyn + wave * 4 * xs;
-  const int nx = (xs - 4) / 64;  // 1 KB loads per token
-  for (int t = 0; t < 4; ++t)
-    for (int d = 0; d < nx; ++d) {
-      const uint32_t c = static_cast<uint32_t>(d) * 64 + lane;
-      const uint32_t k = k0 + c * 8;
-      bload16_lds(rx, xw + t * xs + d * 64,
-                  off_if(c < static_cast<uint32_t>(npc) * 16 && k < static_cast<uint32_t>(p.K) && t < p.M,
-                         static_cast<uint32_t>(t) * ldx_bytes + k * 2));
-    }
-  __builtin_amdgcn_sched_barrier(0);
-
-  auto issue = [&](u32x4 (&w)[R][NQ], int r) {
+  auto issue = [&](u32x4 (&w)[R][NQ], u32x4 (&x)[R][G], int r) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int pc = r * R + i;  // piece within the wave
+      // K % 16 == 0: the lane's 8 k are all in the row or all past its end
+      const uint32_t k = k0 + pc * 128 + 8 * blk;
+      const bool ok = pc < npc && k < static_cast<uint32_t>(p.K);
+#pragma unroll
+      for (int g = 0; g < G; ++g) x[i][g] = bload16(rx, off_if(ok && xok[g], xo[g] + k * 2));
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-        w[i][q] = bload16_nt(rw, off_if(rv[q] && pc < npc,
-                                        static_cast<uint32_t>(row[q]) * row_bytes + (k0 + pc * 128 + 8 * blk) * 2));
+        w[i][q] = bload16_nt(rw, off_if(ok && rv[q], static_cast<uint32_t>(row[q]) * row_bytes + k * 2));
     }
   };
-  f32x4 acc[NQ][1];
+  f32x4 acc[NQ][G];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) acc[q][0] = f32x4{0, 0, 0, 0};
-  auto compute = [&](const u32x4 (&w)[R][NQ], int r) {
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const u32x4 xa = xw[jr * xs + (r * R + i) * 16 + blk];
+    for (int g = 0; g < G; ++g) acc[q][g] = f32x4{0, 0, 0, 0};
+  auto compute = [&](const u32x4 (&w)[R][NQ], const u32x4 (&x)[R][G]) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        acc[q][0] = mfma_4x4x4(u32x2{xa.x, xa.y}, u32x2{w[i][q].x, w[i][q].y}, acc[q][0]);
-        acc[q][0] = mfma_4x4x4(u32x2{xa.z, xa.w}, u32x2{w[i][q].z, w[i][q].w}, acc[q][0]);
-      }
-    }
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          acc[q][g] = mfma_4x4x4(u32x2{x[i][g].x, x[i][g].y}, u32x2{w[i][q].x, w[i][q].y}, acc[q][g]);
+          acc[q][g] = mfma_4x4x4(u32x2{x[i][g].z, x[i][g].w}, u32x2{w[i][q].z, w[i][q].w}, acc[q][g]);
+        }
   };
-  u32x4 wa[R][NQ], wb[R][NQ];
-  issue(wa, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  vm_wait<R * NQ>();  // the activation loads (issued first) are in LDS
-  for (int r = 0; r < rounds; r += 2) {
-    if (r + 1 < rounds) issue(wb, r + 1);
-    compute(wa, r);
-    if (r + 1 >= rounds) break;
-    if (r + 2 < rounds) issue(wa, r + 2);
-    compute(wb, r + 1);
+  if constexpr (ONE) {
+    u32x4 wa[R][NQ], xa[R][G];
+    issue(wa, xa, 0);
+    __builtin_amdgcn_sched_barrier(0);  // every load before any product
+    compute(wa, xa);
+  } else {
+    u32x4 wa[R][NQ], xa[R][G], wb[R][NQ], xb[R][G];
+    issue(wa, xa, 0);
+    for (int r = 0; r < rounds; r += 2) {
+      if (r + 1 < rounds) issue(wb, xb, r + 1);
+      compute(wa, xa);
+      if (r + 1 >= rounds) break;
+      if (r + 2 < rounds) issue(wa, xa, r + 2);
+      compute(wb, xb);
+    }
   }
-  blk_finish<1, NQ, KS, false>(p, acc, row, rv, 1.0f, lane, wave, kw);
+  blk_finish<G, NQ, KS, false>(p, acc, row, rv, 1.0f, lane, wave, kw);
 }
 
 // ------------------------------------------------------------------ MFMA
@@ -1291,6 +1296,7 @@ constexpr int64_t kValuMaxMFp4 = 2;
 // 4 waves (K <= 4096), up to 8 tokens (two groups of 4).
 constexpr int64_t kBlkMaxK = 4096;
 constexpr int64_t kBlkMaxM = 8;
+constexpr int64_t kBlkhMaxM = 8;  // BF16 weights: two groups of 4 tokens
 
 // NVFP4 rows of at most kVchunkMaxK columns: 8-k chunks, at most 8 per lane
 // and 4 waves per unit.
@@ -1486,36 +1492,35 @@ hipError_t launch_blk(const GemvParams& p, hipStream_t stream) {
   }
 }
 
-// BF16 rows of up to kBlkhMaxK columns: at most 28 pieces of 128 k per
-// wave, whose 1 KB activation loads (7 per token) and two rounds of 4 pieces
-// (32 weight loads at 4 groups) stay within vmcnt's count, and whose staged
-// activations (4 tokens x 4 waves x 7 KB) fit the LDS of a compute unit.
-constexpr int kBlkhRound = 4;
-constexpr int64_t kBlkhMaxK = 14336;
-
-template <int NQ>
-hipError_t launch_blkh_nq(GemvParams p, hipStream_t stream) {
+template <int G, int NQ, int R, bool ONE>
+hipError_t launch_blkh_r(GemvParams p, hipStream_t stream) {
   constexpr int KS = 4;
   p.units = (p.units + NQ - 1) / NQ;
   if (t_describe) {
-    std::snprintf(t_describe, t_describe_len, "k_gemv_blkh<%d, %d, %d>", NQ, kBlkhRound, KS);
+    std::snprintf(t_describe, t_describe_len, "k_gemv_blkh<%d, %d, %d, %d, %s>", G, NQ, R, KS, tf(ONE));
     return hipSuccess;
   }
-  const int64_t pw = ((p.K + 127) / 128 + KS - 1) / KS;                         // pieces per wave
-  const int64_t chunks = (pw + kBlkhRound - 1) / kBlkhRound * kBlkhRound * 16;  // 16 per piece
-  const int xs = static_cast<int>((chunks + 63) / 64 * 64 + 4);
-  const size_t lds = static_cast<size_t>(4) * 4 * xs * 16;
-  hipLaunchKernelGGL((k_gemv_blkh<NQ, kBlkhRound, KS>), dim3(static_cast<unsigned>(p.units)), dim3(256), lds, stream,
-                     p, xs);
+  hipLaunchKernelGGL((k_gemv_blkh<G, NQ, R, KS, ONE>), dim3(static_cast<unsigned>(p.units)), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
+// Up to 8 pieces of 128 k per wave (K <= 4096): all loaded up front.
+template <int G, int NQ>
+hipError_t launch_blkh_nq(const GemvParams& p, hipStream_t stream) {
+  const int64_t pw = ((p.K + 127) / 128 + 3) / 4;  // pieces per wave
+  if (pw <= 4) return launch_blkh_r<G, NQ, 4, true>(p, stream);
+  if (pw <= 8) return launch_blkh_r<G, NQ, 8, true>(p, stream);
+  return launch_blkh_r<G, NQ, 4, false>(p, stream);
+}
+
+template <int G>
 hipError_t launch_blkh(const GemvParams& p, hipStream_t stream) {
   switch (blk_quads_per_unit(p.units)) {
-    case 1: return launch_blkh_nq<1>(p, stream);
-    case 2: return launch_blkh_nq<2>(p, stream);
-    case 3: return launch_blkh_nq<3>(p, stream);
-    default: return launch_blkh_nq<4>(p, stream);
+    case 1: return launch_blkh_nq<G, 1>(p, stream);
+    case 2: return launch_blkh_nq<G, 2>(p, stream);
+    case 3: return launch_blkh_nq<G, 3>(p, stream);
+    default: return launch_blkh_nq<G, 4>(p, stream);
   }
 }
 
@@ -1530,7 +1535,8 @@ hipError_t dispatch(GemvParams p, int path, hipStream_t stream) {
       return launch_blk<2, SILU>(p, stream);
     } else if constexpr (!SILU) {
       p.units = (p.N + 3) / 4;  // groups of 4 consecutive rows
-      return launch_blkh(p, stream);
+      if (p.M <= 4) return launch_blkh<1>(p, stream);
+      return launch_blkh<2>(p, stream);
     }
   }
   if (path == kPathValu) {
@@ -1624,9 +1630,8 @@ SplitPlan gemv_split_plan(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
 // NVFP4: the VALU kernel at one token (and at two for rows longer than
 // kBlkMaxK columns), the 4x4 block MFMA kernel from 2 to 4 tokens (rows of
 // up to kBlkMaxK columns), the 16x16 MFMA kernels above.  BF16 without
-// silu_mul: the 4x4 block kernel from 1 to 4 tokens (rows of up to kBlkhMaxK
-// columns), else the MFMA kernels, or the VALU kernel at one token beyond
-// 8192 columns.  NVFP4 rows of up
+// silu_mul: the 4x4 block kernel from 1 to 4 tokens, and from 5 to 8 for
+// rows longer than 2048 columns, else the MFMA kernels.  NVFP4 rows of up
 // to kVchunkMaxK columns take the chunked VALU kernel (M <= 4 when forced);
 // other VALU cases stage M <= 2 activation rows in a 64 KB LDS area.
 // W4A16_GEMV_PATH=valu|mfma|blk forces a path where it applies (the tests
@@ -1637,7 +1642,7 @@ bool valu_fits(bool fp4, int64_t M, int64_t K) {
   return (fp4 && K <= kVchunkMaxK) ? M <= 4 : (M <= 2 && M * ((K + 63) / 64 * 64) * 2 <= 65536);
 }
 bool blk_fits(bool fp4, int64_t M, int64_t K, int silu) {
-  return fp4 ? (K <= kBlkMaxK && M <= kBlkMaxM) : (!silu && K <= kBlkhMaxK && M <= 4);
+  return fp4 ? (K <= kBlkMaxK && M <= kBlkMaxM) : (!silu && M <= kBlkhMaxM);
 }
 
 }  // namespace
@@ -1649,10 +1654,13 @@ int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
   // 14.4, 4 tokens 4.86 / 6.51 / 19.9 (16x16 MFMA) -> 4.42 / 5.58 / 14.9; at
   // 5..8 tokens the 16x16 MFMA kernels stay ahead (4x4x4 MFMAs are a
   // quarter of their rate per product, and 8 tokens' activations halve the
-  // workgroups per compute unit).  BF16 weights, 1..4 tokens (4096 x 4096 /
-  // 4096 x 14336 / 1024 x 14336): 1 token 7.95 / 23.5 (VALU) -> 7.77 / 20.8,
-  // 4 tokens 8.26 / 25.0 / 22.0 (16x16 MFMA) -> 7.92 / 21.0 / 9.0
+  // workgroups per compute unit).  BF16 weights (4096 x 4096 / 4096 x 14336
+  // / 2048 x 8192): 1 token 7.95 / 23.5 / - (VALU) -> 7.08 / 19.9 / 8.2, 4
+  // tokens 8.26 / 25.0 / - (16x16 MFMA) -> 7.59 / 21.3 / 8.9; 8 tokens, rows
+  // longer than 2048 columns, 8.74 / 26.5 / 14.6 (16x16 MFMA) -> 8.37 / 23.8
+  // / 10.6 (at 2048 columns equal, at 1024 4.41 -> 4.71)
   if (blk_fits(fp4, M, K, silu) && M >= (fp4 ? 2 : 1) && M <= 4) return kPathBlk;
+  if (!fp4 && blk_fits(fp4, M, K, silu) && K > 2048) return kPathBlk;
   // NVFP4 without silu_mul at 5..8 tokens: the 4x4 kernel where its units fill
   // the compute units in one round (4096 x 4096: 5.13 -> 5.00 us at 8 tokens;
   // at 6144 x 4096, two units per compute unit, 6.43 -> 6.72)
@@ -1661,8 +1669,9 @@ int default_gemv_path(bool fp4, int64_t M, int64_t N, int64_t K, int silu) {
     const int nq = blk_quads_per_unit(quads);
     if ((quads + nq - 1) / nq <= device_cu_count()) return kPathBlk;
   }
-  // BF16 at M = 1: the MFMA path up to K = 8192 (measured 5% faster at
-  // 4096), the VALU path beyond (2% faster at 14336)
+  // BF16 with silu_mul at M = 1: the MFMA path up to K = 8192 (measured 5%
+  // faster at 4096 without silu_mul), the VALU path beyond (2% faster at
+  // 14336)
   const int64_t valu_max_m = fp4 ? kValuMaxMFp4 : (K <= 8192 ? 0 : 1);
   return (valu_fits(fp4, M, K) && M <= valu_max_m) ? kPathValu : kPathMfma;
 }
