@@ -622,7 +622,7 @@ __global__ __launch_bounds__(256) void k_gemv_blk(const GemvParams p) {
 // into the A operands: lane 4b+i of token group g loads token 4g+i's same 8
 // k (one load of the wave reads 256 contiguous bytes of each of 4 token rows),
 // so neither K nor the token count is bound by LDS (staging them in LDS, as
-// the NVFP4 kernel must, measured 0.4-0.8 us slower).  G groups of 4 tokens;
+// the NVFP4 kernel must, measured up to 1 us slower).  G groups of 4 tokens;
 // the KS waves split the pieces.  ONE: a wave's pieces (at most R) are all
 // loaded up front and multiplied in order as they arrive; else R pieces per
 // round, the next round's weights and activations in flight while the
