@@ -439,6 +439,25 @@ def test_moe_scale_buffers_4_byte_aligned(m):
     moe_check(wts, tok, act.cpu(), sact.cpu(), to_bits(out.cpu()), list(range(m)), f"moe 4-byte scales M={m}")
 
 
+@pytest.mark.parametrize("m", [3, 7])
+@pytest.mark.parametrize("k", [1040, 2560, 5120])
+def test_bf16_gemv_block_kernel_strided_activations(m, k, monkeypatch):
+    """The BF16 4x4 block kernel (forced) reads its activations straight from
+    x: a row stride past K (ldx = K + 64), one and two token groups, every
+    wave's pieces up front (K = 1040, 2560) and in rounds (K = 5120)."""
+    monkeypatch.setenv("W4A16_GEMV_PATH", "blk")
+    n = 272
+    assert lib.gemv_kernel_name(m, n, k, weight_fp4=False).startswith(f"k_gemv_blkh<{1 if m <= 4 else 2},")
+    b = synth.dense_bf16(m, n, k, seed=97 + m + k)
+    wide = torch.zeros((m, k + 64), dtype=torch.bfloat16)
+    wide[:, :k] = b["x"]
+    wide[:, k:] = float("nan")  # never read
+    xv = dev(wide)[:, :k]
+    out = to_bits(lib.bf16_gemv(xv, dev(b["w"])).cpu())
+    _, acc, absacc = oracle.bf16_gemv(b["x"], b["w"])
+    check_gemv(out, acc, absacc, 1.0, k, f"strided x bf16 blkh M={m} K={k}")
+
+
 @pytest.mark.parametrize("m", [1, 2, 5, 17, 40])
 def test_gemv_row_strided_activations_every_family(m):
     """x with a row stride past K (ldx = K + 64) on each kernel family: the
