@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void k_gemv_blkh(const GemvParams p) {
           acc[q][g] = mfma_4x4x4(u32x2{x[i][g].z, x[i][g].w}, u32x2{w[i][q].z, w[i][q].w}, acc[q][g]);
         }
   };
-  if constexpr (ONE) {
+  if constexpr (ONE) {  // the launcher picks it only when pw <= R
     u32x4 wa[R][NQ], xa[R][G];
     issue(wa, xa, 0);
     __builtin_amdgcn_sched_barrier(0);  // every load before any product

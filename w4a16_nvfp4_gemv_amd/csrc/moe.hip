@@ -232,7 +232,6 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
   const int units_r = (p.I + 127) / 128 * 32;
   const int units_s = (p.SI + 127) / 128 * 32;
   const int items_s = p.M * units_s;
-  const int items = P * units_r + items_s;
   const uint32_t nch = p.H / 8;
   const int nkb = static_cast<int>((nch + KS * C * 64 - 1) / (KS * C * 64));
   const uint32_t shift = 8u * ((lane >> 1) & 3);
@@ -313,7 +312,12 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_pairs(const MoeGateUpParams
     __syncthreads();
   };
 
-  for (int item = xcd_logical_block(); item < items; item += gridDim.x) {
+  // The grid is exactly one workgroup per item, so no loop or range check
+  // stands between the kernel arguments and the first loads (with a loop
+  // over items, the expert id's load waited behind the loop's entry test:
+  // 0.3-0.5 us slower at one token).
+  {
+    const int item = xcd_logical_block();
     if (item < items_s) {
       const int t = item / units_s;
       const int u = item - t * units_s;
@@ -370,7 +374,12 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
   const uint32_t sact_bytes = static_cast<uint32_t>(p.M) * p.SI * 2;
   bool tw_stored = false;
 
-  for (int64_t u = xcd_logical_block(); u < units; u += gridDim.x) {
+  // At most one workgroup per unit, so the first unit is this workgroup's
+  // without a test: with the test ahead of the body, the compiler moved the
+  // id and routing-weight loads behind it and three waits for kernel
+  // arguments (0.2 us at one token).
+  int64_t u = xcd_logical_block();
+  do {
     int64_t rows[R];
     bool rv[R];
     quad_rows<R>(u, p.H, 0, rows, rv);
@@ -453,7 +462,8 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down_pairs(const MoeDownParams 
       }
     }
     __syncthreads();
-  }
+    u += gridDim.x;
+  } while (u < units);
 }
 
 // ------------------------------------------------------------------ MFMA forms
@@ -923,8 +933,9 @@ hipError_t launch_moe_gate_up(MoeGateUpParams p, hipStream_t stream) {
     else hipLaunchKernelGGL((k_moe_gate_up_mfma<8>), grid, block, 0, stream, p);
     return hipGetLastError();
   }
-  // one item per workgroup (a persistent grid of 1280 or 2560 workgroups
-  // measured 1.6 / 3.7 us slower at one token); the 4 waves' 8-k chunks
+  // exactly one item per workgroup, which the kernel relies on (a persistent
+  // grid of 1280 or 2560 workgroups measured 1.6 / 3.7 us slower at one
+  // token); the 4 waves' 8-k chunks
   // cover H in one block up to 2048 columns with one chunk per lane
   const int64_t items =
       static_cast<int64_t>(pairs) * ((p.I + 127) / 128 * 32) + static_cast<int64_t>(p.M) * ((p.SI + 127) / 128 * 32);
@@ -954,7 +965,7 @@ hipError_t launch_moe_down_combine(MoeDownParams p, hipStream_t stream) {
   const int sg_max = cl == 1 ? 9 : 4;
   const int sg = jobs < sg_max ? jobs : sg_max;
   const int64_t units = (p.H + 127) / 128 * 32;
-  const dim3 grid(static_cast<unsigned>(units < 8192 ? units : 8192));
+  const dim3 grid(static_cast<unsigned>(units < 8192 ? units : 8192));  // never more than units
   return launch_down_pairs(p, nw, cl, sg, grid, stream);
 }
 
