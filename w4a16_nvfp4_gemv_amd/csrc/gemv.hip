@@ -846,7 +846,11 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
     sxo[i] = t < p.M ? static_cast<uint32_t>(t) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
   }
 
-  for (int64_t item = xcd_logical_block(); item < p.units * S; item += gridDim.x) {
+  // The grid never exceeds the items, so the first item is taken without a
+  // test: a loop test ahead of the body held the first loads behind another
+  // wait for kernel arguments (4096x4096 at 16 tokens 6.26 -> 6.15 us).
+  int64_t item = xcd_logical_block();
+  do {
     const int64_t split = S == 1 ? 0 : item / p.units;
     const int64_t tile = S == 1 ? item : item - split * p.units;  // the unit of RT row tiles
     const int64_t s_first = split * sps;                          // this split's steps
@@ -1039,7 +1043,8 @@ __global__ __launch_bounds__(mfma_waves(XT) * 64) void k_gemv_mfma(const GemvPar
       }
     }
     __syncthreads();
-  }
+    item += gridDim.x;
+  } while (item < p.units * S);
 }
 
 // ------------------------------------------------------------------ MFMA, block-diagonal (NVFP4, M <= 8)
@@ -1117,7 +1122,8 @@ __global__ __launch_bounds__(kBdWaves * 64) void k_gemv_mfma_bd(const GemvParams
     sxo[q] = n < p.M ? static_cast<uint32_t>(n) * static_cast<uint32_t>(p.ldx) * 2 : kOutOfRange;
   }
 
-  for (int64_t unit = xcd_logical_block(); unit < p.units; unit += gridDim.x) {
+  {  // the grid is exactly one workgroup per unit (no test ahead of the first loads)
+    const int64_t unit = xcd_logical_block();
     int64_t rows[NG];
     bool rv[NG];
 #pragma unroll
@@ -1352,7 +1358,7 @@ hipError_t launch_mfma_rt(GemvParams p, hipStream_t stream) {
     return hipSuccess;
   }
   int64_t blocks = p.units * S;
-  if (blocks > 65536) blocks = 65536;
+  if (blocks > 65536) blocks = 65536;  // never more than the items (the kernel relies on it)
   hipLaunchKernelGGL((k_gemv_mfma<FP4, XT, SILU, RT, S>), dim3(static_cast<unsigned>(blocks)),
                      dim3(mfma_waves(XT) * 64), 0, stream, p);
   return hipGetLastError();
@@ -1389,6 +1395,7 @@ bool launch_mfma_bd(GemvParams p, hipStream_t stream, hipError_t* err) {
     *err = hipSuccess;
     return true;
   }
+  // exactly one workgroup per unit: the kernel relies on it
   hipLaunchKernelGGL((k_gemv_mfma_bd<SILU, TK, R>), dim3(static_cast<unsigned>(units)), dim3(kBdWaves * 64), 0,
                      stream, p);
   *err = hipGetLastError();
