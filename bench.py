@@ -448,8 +448,11 @@ def dispatch_table() -> int:
                 rec[path] = {"kernel": kern, "us": round(sorted(us[path])[1], 3)}
             del graphs
             os.environ.pop("W4A16_GEMV_PATH", None)
-            times = [rec[p]["us"] for p in ("valu", "mfma", "blk") if rec[p]]
-            rec["default_is_fastest_path"] = rec["default"]["us"] <= min(times) * 1.02
+            fastest = min((rec[p] for p in ("valu", "mfma", "blk") if rec[p]), key=lambda r: r["us"])
+            # the default picks the fastest family when it runs that family's kernel,
+            # or one within 2% of it (the same kernel timed twice differs by noise)
+            rec["default_is_fastest_path"] = (rec["default"]["kernel"] == fastest["kernel"]
+                                              or rec["default"]["us"] <= fastest["us"] * 1.02)
             best_default += rec["default_is_fastest_path"]
             rows.append(rec)
             print(json.dumps(rec), flush=True)
