@@ -730,6 +730,19 @@ def test_moe_up_to_four_tokens_k_extents(m, h, inter, si):
     moe_check(wts, tok, act, sact, out, list(range(m)), f"moe K extents M={m} H={h} I={inter} SI={si}")
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_moe_more_row_quads_than_workgroups(m):
+    """H = 33024: 8256 quads of H rows, more than the 8192 workgroups of the
+    one-job-per-pair down_combine, so some workgroups take a second quad
+    (its unit loop); gate_up's rows are 33024 columns long (9 K blocks)."""
+    e, topk, h, inter, si = 4, 2, 33024, 64, 64
+    wts = synth.moe_weights(e, h, inter, si, seed=395 + m)
+    tok = synth.moe_tokens(m, h, e, topk, seed=396 + m)
+    _say("moe many quads", m, h)
+    act, sact, out = moe_run(wts, tok, m, topk, inter, si, h)
+    moe_check(wts, tok, act, sact, out, list(range(m)), f"moe many quads M={m}")
+
+
 @pytest.mark.parametrize("m,topk", [(4, 16), (5, 16), (8, 16), (9, 16)])
 def test_moe_most_pairs_of_the_pair_forms(m, topk):
     """The token counts around the limits of the one-job-per-pair forms:
