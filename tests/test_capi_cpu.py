@@ -233,6 +233,7 @@ def test_gemv_kernel_name_query(monkeypatch):
         assert gemv_kernel_name(m, 4096, 4096, weight_fp4=False) == "k_gemv_blkh<2, 4, 8, 4, true>"
         assert gemv_kernel_name(m, 2048, 8192, weight_fp4=False) == "k_gemv_blkh<2, 2, 4, 4, false>"
         assert gemv_kernel_name(m, 4096, 2048, weight_fp4=False).startswith("k_gemv_mfma<false, 8, false,")
+        assert gemv_kernel_name(m, 4096, 2064, weight_fp4=False) == "k_gemv_blkh<2, 4, 8, 4, true>"  # K > 2048
     assert gemv_kernel_name(9, 4096, 4096, weight_fp4=False).startswith("k_gemv_mfma<false, 16, false,")
     assert gemv_kernel_name(4, 4096, 4096, weight_fp4=False, silu_mul=True).startswith("k_gemv_mfma<false, 4, true,")
     assert gemv_kernel_name(1, 8192, 16384, weight_fp4=False, silu_mul=True).startswith("k_gemv_valu<false, 1, 64, true,")
