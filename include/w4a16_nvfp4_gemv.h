@@ -6,10 +6,11 @@
  * hipStream_t; NULL means the legacy default stream) and returns a status
  * code.  No entry point synchronizes the stream or aborts: a call that
  * cannot run returns a non-zero status and enqueues nothing.  No entry point
- * allocates device memory, with one exception: the first nvfp4_dequant_gemm
- * call on a device creates that device's rocBLAS handle, which holds
- * rocBLAS's own device memory until the process ends (make that first call
- * outside HIP graph capture).  All buffers are owned by the caller and must
+ * allocates device memory, with one exception: nvfp4_dequant_gemm runs its
+ * GEMM through rocBLAS, whose handle (created on the first call on a device,
+ * kept until the process ends) manages device memory of its own and may
+ * grow it for larger shapes (make those calls outside HIP graph capture).
+ * All buffers are owned by the caller and must
  * stay alive until the enqueued work has finished.
  *
  * Data formats (the "ModelOpt layout" of the pages vllm.models.flint.ops.

@@ -1,8 +1,9 @@
 // C ABI of the library: argument validation, path choice and launch.
 // No entry point synchronizes or aborts; a call that cannot run returns a
 // non-zero status and enqueues nothing.  None allocates device memory except
-// nvfp4_dequant_gemm, whose first call on a device creates that device's
-// rocBLAS handle (rocBLAS's own device memory, kept until the process ends).
+// nvfp4_dequant_gemm, through rocBLAS: its handle (created on the first call
+// on a device, kept until the process ends) manages device memory of its own
+// and may grow it for larger shapes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
